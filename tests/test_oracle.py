@@ -1,0 +1,323 @@
+"""Pins for the CPU oracle: closed forms, invariants, brute force and
+independent library routines. None of these re-types the oracle's formula."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+import oracle
+from oracle import recurrence as rec_mod
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+MASK_CASES = [("none", None), ("causal", None), ("sliding", 1), ("sliding", 3), ("sliding", 7)]
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ----------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("mask,window", MASK_CASES)
+def test_probability_rows_sum_to_one(mask, window):
+    q, k = _rand((23, 8), 1), _rand((23, 8), 2)
+    p = oracle.probabilities(q, k, 0.7, mask, window)
+    assert np.all(np.abs(p.sum(axis=1) - 1.0) <= 1e-12)
+    vis = oracle.visible(mask, 23, 23, window)
+    assert np.all(p[~vis] == 0.0)
+    assert np.all(p[vis] > 0.0)
+
+
+@pytest.mark.parametrize("mask,window", MASK_CASES)
+def test_equal_scores_give_mean_of_visible_values(mask, window):
+    n, d = 19, 5
+    q = _rand((n, d), 3)
+    k = np.zeros((n, d))                      # every score is 0
+    v = _rand((n, d), 4)
+    o, _ = oracle.attention(q, k, v, 0.5, mask, window)
+    csum = np.vstack([np.zeros((1, d)), np.cumsum(v, axis=0)])
+    for i in range(n):
+        if mask == "none":
+            lo, hi = 0, n
+        elif mask == "causal":
+            lo, hi = 0, i + 1
+        else:
+            lo, hi = max(0, i - window + 1), i + 1
+        want = (csum[hi] - csum[lo]) / (hi - lo)
+        assert np.allclose(o[i], want, rtol=0, atol=1e-13)
+
+
+def test_dominant_score_returns_that_value_row():
+    n, d, scale, a = 64, 8, 0.125, 20.0       # a^2*scale - ln n = 50 - 4.2 > 40
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((n, d))
+    k[:, 0] = 0.0
+    j_star = 37
+    k[j_star] = 0.0
+    k[j_star, 0] = a
+    q = np.zeros((n, d))
+    q[:, 0] = a
+    v = rng.standard_normal((n, d))
+    o, _ = oracle.attention(q, k, v, scale, "none")
+    assert np.max(np.abs(o - v[j_star][None, :])) <= 1e-15 * np.max(np.abs(v))
+
+
+def test_causal_row_zero_is_first_value_row():
+    q, k, v = _rand((9, 4), 6), _rand((9, 4), 7), _rand((9, 4), 8)
+    o, _ = oracle.attention(q, k, v, 0.3, "causal")
+    assert np.array_equal(o[0], v[0])
+    o, _ = oracle.attention(q, k, v, 0.3, "sliding", window=1)
+    assert np.array_equal(o, v)               # window 1: each query sees only itself
+
+
+def test_single_key_and_two_key_closed_forms():
+    q, k, v = _rand((1, 3), 9), _rand((1, 3), 10), _rand((1, 3), 11)
+    o, lse = oracle.attention(q, k, v, 0.9, "none")
+    assert np.array_equal(o[0], v[0])
+    assert abs(lse[0] - 0.9 * float(q[0] @ k[0])) <= 1e-15
+    # d = 1, two keys: O = sigma(s0 - s1) v0 + sigma(s1 - s0) v1
+    q, k, v = np.array([[0.7]]), np.array([[1.3], [-0.4]]), np.array([[2.0], [-5.0]])
+    s0, s1 = 0.7 * 1.3 * 0.6, 0.7 * -0.4 * 0.6
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    want = sig(s0 - s1) * 2.0 + sig(s1 - s0) * -5.0
+    o, _ = oracle.attention(q, k, v, 0.6, "none")
+    assert abs(o[0, 0] - want) <= 1e-14
+
+
+def test_invariances_without_mask():
+    n, d = 17, 6
+    q, k, v = _rand((n, d), 12), _rand((n, d), 13), _rand((n, d), 14)
+    o, _ = oracle.attention(q, k, v, 0.4, "none")
+    u = _rand((d,), 15)
+    o_shift, _ = oracle.attention(q, k + u[None, :], v, 0.4, "none")
+    assert np.max(np.abs(o_shift - o)) <= 1e-12
+    perm = np.random.default_rng(16).permutation(n)
+    o_perm, _ = oracle.attention(q, k[perm], v[perm], 0.4, "none")
+    assert np.max(np.abs(o_perm - o)) <= 1e-12
+    o_aff, _ = oracle.attention(q, k, 3.0 * v - 2.0, 0.4, "none")
+    assert np.max(np.abs(o_aff - (3.0 * o - 2.0))) <= 1e-12
+
+
+@pytest.mark.parametrize("mask,window", MASK_CASES)
+def test_matches_torch_sdpa_float64(mask, window):
+    B, H, n, d = 2, 3, 37, 16
+    q, k, v = _rand((B, H, n, d), 17), _rand((B, H, n, d), 18), _rand((B, H, n, d), 19)
+    scale = 1.0 / math.sqrt(d)
+    o, _ = oracle.attention(q, k, v, scale, mask, window)
+    vis = torch.from_numpy(oracle.visible(mask, n, n, window))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=vis, scale=scale)
+    assert np.max(np.abs(o - ref.numpy())) <= 1e-12
+
+
+@pytest.mark.parametrize("mask,window", MASK_CASES)
+def test_lse_matches_scipy_logsumexp(mask, window):
+    n, d = 21, 4
+    q, k, v = _rand((n, d), 20), _rand((n, d), 21), _rand((n, d), 22)
+    _, lse = oracle.attention(q, k, v, 1.1, mask, window)
+    s = (q @ k.T) * 1.1
+    s[~oracle.visible(mask, n, n, window)] = -np.inf
+    assert np.max(np.abs(lse - logsumexp(s, axis=1))) <= 1e-12
+
+
+def test_row_subset_and_query_offset():
+    n, d = 40, 8
+    q, k, v = _rand((n, d), 23), _rand((n, d), 24), _rand((n, d), 25)
+    o_full, lse_full = oracle.attention(q, k, v, 0.3, "sliding", 9)
+    rows = [0, 5, 39, 17]
+    o_rows, lse_rows = oracle.attention(q, k, v, 0.3, "sliding", 9, rows=rows)
+    assert np.array_equal(o_rows, o_full[rows]) and np.array_equal(lse_rows, lse_full[rows])
+    o_last, _ = oracle.attention(q[-1:], k, v, 0.3, "causal", q_pos_offset=n - 1)
+    o_causal, _ = oracle.attention(q, k, v, 0.3, "causal")
+    assert np.max(np.abs(o_last[0] - o_causal[-1])) <= 1e-14
+
+
+# ----------------------------------------------------------------- masks
+
+def test_visible_pair_counts_match_closed_forms():
+    with open(os.path.join(GOLDEN, "visible_pairs.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        assert oracle.visible_pair_count(c["mask"], c["n"], c["window"]) == c["pairs"]
+        if c["n"] <= 4096:
+            got = int(oracle.visible(c["mask"], c["n"], c["n"], c["window"]).sum())
+            assert got == c["pairs"]
+
+
+def test_mask_structure():
+    for n in range(1, 30):
+        causal = oracle.visible("causal", n, n)
+        assert np.array_equal(causal, np.tril(np.ones((n, n), dtype=bool)))
+        assert np.array_equal(oracle.visible("sliding", n, n, n), causal)
+        assert np.array_equal(oracle.visible("sliding", n, n, n + 5), causal)
+        assert np.array_equal(oracle.visible("sliding", n, n, 1), np.eye(n, dtype=bool))
+        for w in range(1, n + 2):
+            band = np.tril(np.ones((n, n), dtype=bool)) & ~np.tril(np.ones((n, n), dtype=bool), -w)
+            assert np.array_equal(oracle.visible("sliding", n, n, w), band)
+
+
+# ----------------------------------------------------------------- recurrence
+
+def _two_pass(q, k, v, scale, mask, window):
+    return oracle.attention(q, k, v, scale, mask, window)[0]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 13, 16, 31, 33])
+@pytest.mark.parametrize("d", [1, 3, 8])
+def test_recurrence_matches_two_pass_every_tiling(n, d):
+    rng = np.random.default_rng(100 + n * 10 + d)
+    q, k, v = (rng.standard_normal((n, d)) * 2 for _ in range(3))
+    for mask, window in [("none", None), ("causal", None), ("sliding", 1), ("sliding", 2),
+                         ("sliding", max(1, n // 2)), ("sliding", n + 1)]:
+        ref = _two_pass(q, k, v, 0.8, mask, window)
+        for bn in sorted(set([1, 2, 3, 4, 7, n, n + 1])):
+            for bm in sorted(set([1, 5, n])):
+                got = oracle.tiled_attention(q, k, v, 0.8, mask, window, bm=bm, bn=bn)
+                assert np.max(np.abs(got - ref)) <= 1e-12, (mask, window, bm, bn)
+
+
+def test_recurrence_all_tile_sizes_small():
+    n, d = 12, 2
+    rng = np.random.default_rng(7)
+    q, k, v = (rng.standard_normal((n, d)) * 3 for _ in range(3))
+    for mask, window in MASK_CASES:
+        ref = _two_pass(q, k, v, 1.0, mask, window)
+        for bn in range(1, n + 2):
+            for bm in range(1, n + 2):
+                got = oracle.tiled_attention(q, k, v, 1.0, mask, window, bm=bm, bn=bn)
+                assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_dropping_the_rescale_breaks_the_result(monkeypatch):
+    """A planted mistake (no exp(m - m_new) rescale) must be caught: equal for
+    a single K tile, wrong once N exceeds the tile size."""
+    n, d = 24, 4
+    rng = np.random.default_rng(8)
+    q, k, v = (rng.standard_normal((n, d)) * 3 for _ in range(3))
+    ref = _two_pass(q, k, v, 1.0, "none", None)
+    monkeypatch.setattr(rec_mod, "_rescale_factor", lambda m_old, m_ref: np.ones_like(m_ref))
+    single = oracle.tiled_attention(q, k, v, 1.0, "none", None, bm=8, bn=n)
+    assert np.max(np.abs(single - ref)) <= 1e-12
+    broken = oracle.tiled_attention(q, k, v, 1.0, "none", None, bm=8, bn=6)
+    assert np.max(np.abs(broken - ref)) > 1e-3
+
+
+@pytest.mark.parametrize("mask,window", MASK_CASES)
+def test_split_and_merge_matches_two_pass(mask, window):
+    n, d = 29, 5
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((n, d)) * 2 for _ in range(3))
+    ref = _two_pass(q, k, v, 0.9, mask, window)
+    for bounds in [(), (1,), (7, 14, 21), (3, 3, 28), tuple(range(1, n))]:
+        got = oracle.split_attention(q, k, v, 0.9, mask, window, bounds=bounds, bn=4)
+        assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+# ----------------------------------------------------------------- paged
+
+def test_paged_gather_round_trip_and_decode():
+    from tiled_attention_amd.workloads import paged_inputs, bf16_to_f64
+    inp = paged_inputs(n_seq=5, H=3, d=8, l_min=1, l_max=70, seed=3, spare=4, keep_dense=True)
+    pool_bits = inp.k_pool.view(torch.int16).numpy()
+    got = oracle.gather(pool_bits, inp.block_table.numpy(), inp.seq_lens.numpy())
+    for s in range(5):
+        want = inp.k_dense[s].view(torch.int16).numpy()
+        assert np.array_equal(got[s], want)           # bit-identical copy
+    vals = oracle.gather(inp.v_pool.float().numpy(), inp.block_table.numpy(), inp.seq_lens.numpy())
+    assert not any(np.isnan(x).any() for x in vals)  # poison never read
+    scale = 1.0 / math.sqrt(8)
+    o, lse = oracle.decode(bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
+                           inp.block_table.numpy(), inp.seq_lens.numpy(), scale)
+    for s in range(5):
+        L = int(inp.seq_lens[s])
+        kd, vd = bf16_to_f64(inp.k_dense[s]), bf16_to_f64(inp.v_dense[s])
+        qd = np.repeat(bf16_to_f64(inp.q)[s][:, None, :], L, axis=1)
+        qfull = np.concatenate([np.zeros((3, L - 1, 8)), qd[:, -1:, :]], axis=1)
+        o_c, lse_c = oracle.attention(qfull, kd, vd, scale, "causal")
+        assert np.max(np.abs(o[s] - o_c[:, -1, :])) <= 1e-12
+        assert np.max(np.abs(lse[s] - lse_c[:, -1])) <= 1e-12
+
+
+def test_paged_layout_shapes_and_poison():
+    from tiled_attention_amd.workloads import paged_inputs
+    inp = paged_inputs(n_seq=4, H=2, d=4, l_min=1, l_max=40, seed=11, spare=3)
+    lens = inp.seq_lens.numpy()
+    pages = (lens + 15) // 16
+    assert inp.k_pool.shape[0] == pages.sum() + 3
+    table = inp.block_table.numpy()
+    used = np.concatenate([table[s, :pages[s]] for s in range(4)])
+    assert len(set(used.tolist())) == used.size          # pages are not shared
+    assert np.all(table[np.arange(table.shape[1])[None, :] >= pages[:, None]] == -1)
+    pool = inp.k_pool.float().numpy()
+    spare = sorted(set(range(pool.shape[0])) - set(used.tolist()))
+    assert np.isnan(pool[spare]).all()
+
+
+# ----------------------------------------------------------------- fp8
+
+def test_e4m3_points_from_the_format_definition():
+    with open(os.path.join(GOLDEN, "e4m3fn_points.json")) as f:
+        g = json.load(f)
+    for code, val in g["points"]:
+        got = float(oracle.e4m3_value(int(code, 16)))
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), code
+    for code in g["nan"]:
+        assert math.isnan(float(oracle.e4m3_value(int(code, 16))))
+    table = oracle.e4m3_table()
+    assert table.size == 127 and np.all(np.diff(table) > 0) and table[-1] == oracle.E4M3_MAX
+
+
+def test_e4m3_encode_round_trip_and_torch_cast():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.e4m3_value(codes).astype(np.float32)
+    enc = oracle.e4m3_encode(vals)
+    # +0 and -0 both decode to 0; -0.0 keeps its sign bit
+    assert np.array_equal(enc, codes)
+    rng = np.random.default_rng(12)
+    y = np.concatenate([
+        rng.uniform(-448, 448, 200000).astype(np.float32),
+        (rng.standard_normal(100000) * 0.01).astype(np.float32),
+        # exact midpoints between neighbouring values: ties
+        ((oracle.e4m3_table()[:-1] + oracle.e4m3_table()[1:]) / 2).astype(np.float32),
+        -((oracle.e4m3_table()[:-1] + oracle.e4m3_table()[1:]) / 2).astype(np.float32),
+    ])
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(y), ref)
+    # saturation above 448 (torch gives NaN there, the reading here saturates)
+    assert oracle.e4m3_encode(np.float32(470.0)) == 0x7E
+    assert oracle.e4m3_encode(np.float32(-1e6)) == 0xFE
+
+
+def test_block_quantisation_properties():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((2, 3, 300, 16)).astype(np.float32)
+    x[0, 1, 130:140] = 0.0
+    x[1, 2, 256:] = 0.0                                   # whole ragged last block zero
+    x[rng.random(x.shape) < 0.01] *= 20
+    codes, scales = oracle.quantize_blocks(x, 128)
+    assert codes.shape == x.shape and scales.shape == (2, 3, 3)
+    for b in range(2):
+        for h in range(3):
+            for r in range(3):
+                blk = x[b, h, r * 128:(r + 1) * 128]
+                cb = codes[b, h, r * 128:(r + 1) * 128]
+                amax = np.abs(blk).max()
+                if amax == 0:
+                    assert scales[b, h, r] == 1.0 and np.all(cb == 0)
+                    continue
+                assert scales[b, h, r] == np.float32(amax) / np.float32(448.0)
+                at_max = np.abs(blk) == amax
+                assert np.all(np.isin(cb[at_max], [0x7E, 0xFE]))
+    xhat = oracle.dequantize_blocks(codes, scales, 128)
+    # per element: |x - xhat| <= half an e4m3 step at |y|, times the scale
+    s = np.repeat(scales.astype(np.float64), 128, axis=-1)[..., :300, None]
+    y = np.abs(x / s)
+    e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+    half_ulp = 0.5 * 2.0 ** (e - 3)
+    assert np.all(np.abs(x - xhat) <= half_ulp * s * (1 + 1e-5) + 1e-30)
+    assert np.all(np.abs(xhat) <= 448.0 * s + 1e-30)

@@ -1,0 +1,163 @@
+"""Seeded synthetic workloads for the attention forward path.
+
+This module only draws random numbers and lays them out; it holds none of
+the attention arithmetic. It is the one module that both the GPU path's
+callers (tests, bench, smoke) and the CPU oracle's callers use, so that both
+sides see the same bytes.
+
+Shapes follow the workloads the pages discuss: seq 8192 / d 128 / 32 heads
+("Flash MSA Attention Kernel Implementation Tutorial", "Performance
+Benchmarks"), a 4096-token window ("Optimizing Triton kernels for custom
+attention patterns on H100", Pattern B), 16-token KV pages (same page,
+Pattern C) and 128-row fp8 blocks with outliers ("FlashAttention-3 ...",
+"FP8 Block Quantization").
+
+Recipe (all draws from ``numpy.random.default_rng(seed)``):
+* dense: Q, K, V drawn in that order, ``standard_normal(shape, float32)``.
+  With outliers, then three masks ``random(shape) < p`` (for Q, K, V in that
+  order) scale the chosen entries by ``outlier_scale``.
+* paged: the sequence lengths ``integers(l_min, l_max, endpoint=True)``, then
+  Q [S, H, d], then per sequence K_s and V_s [H, L_s, d], then a permutation
+  of the P = sum ceil(L_s/16) + spare page ids, handed out in (sequence, slot)
+  order. Unused rows of last pages and spare pages hold NaN; block-table
+  entries past a sequence's last page hold -1.
+* bf16 values are the fp32 draws rounded to nearest-even once, on the host
+  (``torch.Tensor.to(torch.bfloat16)``), before either side sees them.
+"""
+
+from dataclasses import dataclass, field
+import hashlib
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: int
+    name: str
+    kind: str                      # "dense" | "paged" | "fp8"
+    B: int = 1
+    H: int = 1
+    N: int = 1
+    d: int = 64
+    dtype: str = "bf16"            # input dtype of Q/K/V for dense
+    out_dtype: str = "bf16"
+    mask: str = "none"
+    window: int = 0
+    n_seq: int = 0
+    l_min: int = 0
+    l_max: int = 0
+    page_size: int = 16
+    spare_pages: int = 64
+    outlier_p: float = 0.0
+    outlier_scale: float = 1.0
+    qk_block: int = 128
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def scale(self):
+        return 1.0 / float(np.sqrt(self.d))
+
+
+WORKLOADS = {
+    1: Workload(1, "dense_f32_b1_h1_n256_d64", "dense", B=1, H=1, N=256, d=64,
+                dtype="f32", out_dtype="f32", mask="none"),
+    2: Workload(2, "causal_bf16_b4_h16_n2048_d64", "dense", B=4, H=16, N=2048, d=64,
+                mask="causal"),
+    3: Workload(3, "sliding4096_bf16_b2_h32_n8192_d128", "dense", B=2, H=32, N=8192, d=128,
+                mask="sliding", window=4096),
+    4: Workload(4, "paged_decode_bf16_s64_h32_d128_p16_l512to8192", "paged", H=32, d=128,
+                n_seq=64, l_min=512, l_max=8192),
+    5: Workload(5, "fp8_causal_b1_h16_n16384_d128", "fp8", B=1, H=16, N=16384, d=128,
+                mask="causal", outlier_p=0.01, outlier_scale=20.0),
+}
+
+
+def default_seed(key):
+    return 1000 + int(key)
+
+
+def to_bf16(x):
+    """fp32 numpy array -> torch bfloat16 tensor (round to nearest even)."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def bf16_to_f64(t):
+    """Exact upcast of a bf16 torch tensor to a float64 numpy array."""
+    return t.to(torch.float32).numpy().astype(np.float64)
+
+
+def dense_inputs(B, H, N, d, seed, outlier_p=0.0, outlier_scale=1.0):
+    """Q, K, V fp32 arrays [B, H, N, d]."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if outlier_p > 0:
+        for x in (q, k, v):
+            sel = rng.random(shape) < outlier_p
+            x[sel] *= np.float32(outlier_scale)
+    return q, k, v
+
+
+@dataclass
+class PagedInputs:
+    q: torch.Tensor               # [S, H, d] bf16
+    k_pool: torch.Tensor          # [P, H, page, d] bf16
+    v_pool: torch.Tensor
+    block_table: torch.Tensor     # [S, max_pages] int32, -1 padded
+    seq_lens: torch.Tensor        # [S] int32
+    page_size: int
+    k_dense: list = None          # per sequence [H, L_s, d] bf16 (if kept)
+    v_dense: list = None
+
+
+def paged_inputs(n_seq, H, d, l_min, l_max, seed, page_size=16, spare=64, max_pages=None,
+                 keep_dense=False):
+    """A shuffled paged KV pool with per-sequence block tables."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(l_min, l_max, size=n_seq, endpoint=True).astype(np.int64)
+    q = rng.standard_normal((n_seq, H, d), dtype=np.float32)
+    pages_per_seq = (lens + page_size - 1) // page_size
+    if max_pages is None:
+        max_pages = -(-l_max // page_size)
+    n_pages = int(pages_per_seq.sum()) + spare
+    k_pool = torch.full((n_pages, H, page_size, d), float("nan"), dtype=torch.bfloat16)
+    v_pool = torch.full((n_pages, H, page_size, d), float("nan"), dtype=torch.bfloat16)
+    k_dense, v_dense = [], []
+    for s in range(n_seq):
+        ks = rng.standard_normal((H, int(lens[s]), d), dtype=np.float32)
+        vs = rng.standard_normal((H, int(lens[s]), d), dtype=np.float32)
+        k_dense.append(to_bf16(ks))
+        v_dense.append(to_bf16(vs))
+    perm = rng.permutation(n_pages)
+    table = np.full((n_seq, max_pages), -1, dtype=np.int32)
+    cursor = 0
+    for s in range(n_seq):
+        np_s = int(pages_per_seq[s])
+        ids = perm[cursor:cursor + np_s]
+        cursor += np_s
+        table[s, :np_s] = ids
+        length = int(lens[s])
+        for src, pool in ((k_dense[s], k_pool), (v_dense[s], v_pool)):
+            padded = torch.full((H, np_s * page_size, d), float("nan"), dtype=torch.bfloat16)
+            padded[:, :length] = src
+            pool[torch.from_numpy(ids.astype(np.int64))] = padded.view(H, np_s, page_size, d).transpose(0, 1)
+    out = PagedInputs(q=to_bf16(q), k_pool=k_pool, v_pool=v_pool,
+                      block_table=torch.from_numpy(table), seq_lens=torch.from_numpy(lens.astype(np.int32)),
+                      page_size=page_size)
+    if keep_dense:
+        out.k_dense, out.v_dense = k_dense, v_dense
+    return out
+
+
+def tensor_digest(*tensors):
+    """Short hash of the raw bytes of the given CPU tensors / arrays."""
+    h = hashlib.sha256()
+    for t in tensors:
+        if isinstance(t, torch.Tensor):
+            t = t.contiguous().view(torch.uint8).numpy() if t.dtype != torch.uint8 else t.contiguous().numpy()
+        h.update(np.ascontiguousarray(t).tobytes())
+    return h.hexdigest()[:16]
