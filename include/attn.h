@@ -1,0 +1,181 @@
+/*
+ * attn.h -- C ABI of libattn.so, a flash-attention forward library for
+ * AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * The operation (all entry points): for each (batch b, head h),
+ *     O = softmax(Q K^T * scale, masked) V
+ * computed tile by tile with an online softmax so the N x N score matrix is
+ * never stored: "Flash MSA Attention Kernel Implementation Tutorial",
+ * sections "Why We Needed a New Attention Kernel" and "Understanding Flash
+ * MSA Core Mechanics". Scores are accumulated in fp32; the running row max
+ * m and row sum l are fp32.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers (hipMalloc'd or equivalent) unless noted.
+ *     The caller owns every buffer; the library allocates nothing, frees
+ *     nothing and keeps no pointer after returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is only enqueued; the library never synchronises.
+ *   - Every argument is checked on the host before anything is enqueued: a
+ *     return value other than ATTN_OK means no device work was issued and
+ *     no memory was touched (so these paths work without a GPU).
+ *     ATTN_ERR_LAUNCH is the exception: it reports a failed launch.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - Base pointers must be 16-byte aligned. Outputs must not alias inputs.
+ *   - Tensors are dense, row-major, innermost dimension last.
+ *   - Sizes: d (head dim) in {64, 128}; N >= 1; B*H*N < 2^31.
+ *   - No C++ exception crosses this interface; the library holds no state
+ *     and every call is thread-safe.
+ */
+#ifndef TILED_ATTENTION_AMD_ATTN_H
+#define TILED_ATTENTION_AMD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, misalignment, bad enum, window < 1 */
+  ATTN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d = 96, page_size = 64) */
+  ATTN_ERR_WORKSPACE = 3,    /* workspace smaller than the size query returns */
+  ATTN_ERR_LAUNCH = 4        /* the HIP runtime reported a launch failure */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_FP8_E4M3 = 2 } attn_dtype;
+
+/* Visibility of key j to query i (square masks, positions 0..N-1):
+ *   NONE    every key;
+ *   CAUSAL  j <= i;
+ *   SLIDING i - window < j <= i  (one-sided causal window of `window` keys,
+ *           the query included). The window pattern is "Optimizing Triton
+ *           kernels for custom attention patterns on H100", Pattern B. */
+typedef enum { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL = 1, ATTN_MASK_SLIDING = 2 } attn_mask;
+
+/*
+ * attn_fwd -- dense / causal / sliding-window prefill.
+ *   q, k, v : [B, H, N, d], dtype in_dtype (ATTN_F32 or ATTN_BF16, all three alike).
+ *   o       : [B, H, N, d], dtype out_dtype (ATTN_F32 or ATTN_BF16); every
+ *             element is written (a row with no visible key, impossible for
+ *             these masks, would be written as 0).
+ *   scale   : multiplies Q K^T; the pages use 1/sqrt(d) (kernel listing in
+ *             "Flash MSA ...", "Implementation Step-by-Step with Triton").
+ *   mask, window : see attn_mask; window is ignored unless SLIDING (>= 1).
+ *   lse     : NULL, or [B, H, N] fp32 receiving log(sum_j exp(S_ij)) per row
+ *             (natural log, scaled scores), -inf for a row with no visible key.
+ * bf16 inputs run on bf16 MFMA with fp32 accumulation; fp32 inputs run in
+ * fp32 throughout. The K/V loop skips tiles with no visible pair and applies
+ * the mask only on tiles that straddle its edge ("Optimizing Triton kernels
+ * ...", Pattern B).
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
+                     int B, int H, int N, int d,
+                     attn_dtype in_dtype, attn_dtype out_dtype,
+                     float scale, attn_mask mask, int window,
+                     float* lse, void* stream);
+
+/*
+ * attn_fwd_fp8 -- prefill with block-quantised fp8 Q and K and bf16 V
+ * ("FlashAttention-3: Warp Specialization ...", "FP8 Block Quantization").
+ *   q8, k8   : [B, H, N, d] OCP E4M3FN bytes.
+ *   q_scale, k_scale : [B, H, ceil(N/qk_block)] fp32; the value of element
+ *              x is e4m3(code) * scale of its qk_block-row block.
+ *   v        : [B, H, N, d] bf16.   o : [B, H, N, d] bf16.
+ *   S_ij = (sum_k q8_ik k8_jk) * q_scale[i/qk_block] * k_scale[j/qk_block] * scale,
+ *   with the fp8 product accumulated in fp32; the rescale is folded into the
+ *   exponent of the online softmax. P is rounded to bf16 for P V.
+ *   qk_block must be 128. mask/window as in attn_fwd. lse: NULL or [B,H,N].
+ */
+attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale,
+                         const uint8_t* k8, const float* k_scale,
+                         const void* v, void* o,
+                         int B, int H, int N, int d, int qk_block,
+                         float scale, attn_mask mask, int window,
+                         float* lse, void* stream);
+
+/*
+ * attn_quant_fp8_block -- per-block E4M3FN quantisation of x [B, H, N, d] fp32
+ * ("FlashAttention-3 ...", "FP8 Block Quantization"): for every 128-row
+ * block (the last may be ragged) s = fp32(absmax) / 448 (IEEE fp32 division;
+ * s = 1 for an all-zero block), code = e4m3(x / s) rounded to nearest, ties
+ * to even, saturating at +-448.
+ *   codes  : [B, H, N, d] uint8 out.   scales : [B, H, ceil(N/block)] fp32 out.
+ *   block must be 128.
+ */
+attn_status attn_quant_fp8_block(const float* x, uint8_t* codes, float* scales,
+                                 int B, int H, int N, int d, int block, void* stream);
+
+/*
+ * Paged KV cache ("Optimizing Triton kernels ...", Pattern C).
+ *   k_pool, v_pool : [num_pages, H, page_size, d] bf16; page p, head h holds
+ *                    rows t % page_size of the tokens mapped to it.
+ *   block_table    : [S, max_pages] int32 (device); token t of sequence s is
+ *                    in page block_table[s, t / page_size], row t % page_size.
+ *                    Entries at or past ceil(seq_lens[s] / page_size) are
+ *                    never read. Page ids must lie in [0, num_pages): they
+ *                    are not checked on the device (caller's contract).
+ *   seq_lens       : [S] int32 (device), 1 <= seq_lens[s] <= max_pages*page_size.
+ *   page_size must be 16.
+ */
+
+/* Bytes of workspace attn_decode_paged uses to split long sequences. */
+size_t attn_decode_paged_workspace_size(int S, int H, int d, int max_pages, int page_size);
+
+/*
+ * attn_decode_paged -- one new query token per sequence at position
+ * seq_lens[s] - 1, attending to all seq_lens[s] cached keys.
+ *   q, o : [S, H, d] bf16.
+ *   workspace : NULL (each (sequence, head) is one pass over its pages) or at
+ *               least attn_decode_paged_workspace_size(...) bytes (sequences
+ *               are split into page ranges processed in parallel and merged
+ *               with the online-softmax rescale). Smaller -> ATTN_ERR_WORKSPACE.
+ *   lse : NULL or [S, H] fp32.
+ */
+attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* o, int S, int H, int d, int page_size,
+                              int max_pages, int num_pages, float scale,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * attn_gather_paged -- stage one of the two-stage paged route: a bit copy
+ *   k_out[s, h, t, :] = k_pool[block_table[s, t / page_size], h, t % page_size, :]
+ * (same for v) for t < seq_lens[s]. k_out, v_out: [S, H, max_pages*page_size, d]
+ * of `dtype` (ATTN_BF16 or ATTN_F32, element size only); rows t >= seq_lens[s]
+ * are left untouched.
+ */
+attn_status attn_gather_paged(const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* k_out, void* v_out, int S, int H, int d,
+                              int page_size, int max_pages, int num_pages,
+                              attn_dtype dtype, void* stream);
+
+/*
+ * Host-side tile planning (no device access). Tiles of query rows
+ * [m0, m1) against keys [n0, n1) are EMPTY (0: no visible pair, never
+ * loaded), PARTIAL (1: the mask is applied element by element) or FULL
+ * (2: every pair visible, no mask work). Keys >= N do not exist, so a tile
+ * reaching past N is at most PARTIAL; rows >= N are ignored.
+ * Returns -1 on invalid arguments.
+ */
+int attn_tile_class(attn_mask mask, int window, int N, int m0, int m1, int n0, int n1);
+
+/* K-tile index range [*t_lo, *t_hi) (tiles of bn keys) that can hold a key
+ * visible to some row of [m0, m1); tiles outside it are EMPTY. */
+attn_status attn_k_tile_range(attn_mask mask, int window, int N, int m0, int m1, int bn,
+                              int* t_lo, int* t_hi);
+
+const char* attn_status_str(attn_status s);
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILED_ATTENTION_AMD_ATTN_H */

@@ -1,0 +1,63 @@
+"""Helpers shared by the GPU parity tests: tolerances and comparisons.
+
+The tolerances are the stated bars: max-abs 1e-2 for fp32-accumulated bf16
+attention, relative RMSE 5e-2 for the fp8 path, bit-exact for the page
+gather and the quantiser's codes. A bf16 *output* adds its own rounding: half
+a bf16 ulp of the reference value, which alone exceeds 1e-2 once |O| >= 4, so
+bf16-output checks allow 1e-2 + ulp/2 of the reference element.
+"""
+
+import sys
+
+import numpy as np
+import torch
+
+ATOL = 1e-2
+FP8_REL_RMSE = 5e-2
+
+
+def say(*a):
+    """Print a progress line and flush (so a GPU run shows what it was doing)."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def half_ulp_bf16(ref):
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
+def check_close(got, ref, out_bf16, what=""):
+    """max |got - ref| <= 1e-2 (+ half a bf16 ulp of ref for bf16 outputs)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    tol = ATOL + (half_ulp_bf16(ref) if out_bf16 else 0.0)
+    worst = np.unravel_index(np.argmax(err - tol), err.shape)
+    assert np.all(err <= tol), f"{what}: max err {err.max():.3g} at {worst} (ref {ref[worst]:.4g}, tol {tol if np.isscalar(tol) else tol[worst]:.3g})"
+    return float(err.max())
+
+
+def rel_rmse(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.sqrt(np.sum((got - ref) ** 2) / np.sum(ref ** 2)))
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def cuda(t):
+    return t.contiguous().to("cuda")
+
+
+def sample_rows(N, seed, extra=24):
+    """Edge rows (tile boundaries, first, last) plus a seeded random sample."""
+    fixed = {0, 1, 2, 31, 32, 63, 64, 127, 128, 129, N // 2, N - 2, N - 1}
+    rng = np.random.default_rng(seed)
+    rnd = set(rng.integers(0, N, size=extra).tolist())
+    return sorted(r for r in fixed | rnd if 0 <= r < N)

@@ -1,0 +1,116 @@
+"""GPU parity of attn_decode_paged and attn_gather_paged against the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check_close, cuda, say, to_np
+from tiled_attention_amd import _lib as A
+from tiled_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(inp, scale, use_ws):
+    S, H, d = inp.q.shape
+    q, kp, vp = cuda(inp.q), cuda(inp.k_pool), cuda(inp.v_pool)
+    bt, lens = cuda(inp.block_table), cuda(inp.seq_lens)
+    o = torch.full((S, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((S, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = None
+    if use_ws:
+        nbytes = A.attn_decode_paged_workspace_size(S, H, d, bt.shape[1])
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    A.attn_decode_paged(q, kp, vp, bt, lens, o, scale, workspace=ws, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_decode(inp, scale, seqs=None):
+    seqs = list(range(inp.q.shape[0])) if seqs is None else seqs
+    o, lse = oracle.decode(wl.bf16_to_f64(inp.q[seqs]), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
+                           inp.block_table.numpy()[seqs], inp.seq_lens.numpy()[seqs], scale)
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("lens", [(1, 40), (1, 1100)])
+def test_decode_small_elementwise(d, use_ws, lens):
+    say(f"decode d={d} ws={use_ws} lens={lens}")
+    inp = wl.paged_inputs(n_seq=6, H=4, d=d, l_min=lens[0], l_max=lens[1], seed=21 + d + lens[1], spare=5)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _decode(inp, scale, use_ws)
+    ref, ref_lse = _oracle_decode(inp, scale)
+    check_close(to_np(o), ref, True, what=f"decode d={d}")
+    assert np.max(np.abs(to_np(lse) - ref_lse)) <= 1e-3
+
+
+def test_decode_exact_page_multiples_and_single_token():
+    inp = wl.paged_inputs(n_seq=4, H=2, d=128, l_min=1, l_max=1, seed=5, spare=2)
+    o, _ = _decode(inp, 0.1, True)
+    # one key: the output is that key's value row (rounded to bf16 once)
+    v_first = torch.stack([inp.v_pool[int(inp.block_table[s, 0]), :, 0, :] for s in range(4)])
+    assert torch.equal(o.cpu().view(torch.int16), v_first.view(torch.int16))
+    for L in (16, 32, 512, 528):
+        inp = wl.paged_inputs(n_seq=3, H=2, d=128, l_min=L, l_max=L, seed=L, spare=1)
+        o, _ = _decode(inp, 0.1, True)
+        ref, _ = _oracle_decode(inp, 0.1)
+        check_close(to_np(o), ref, True, what=f"L={L}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_gather_bit_exact_small(d):
+    inp = wl.paged_inputs(n_seq=5, H=3, d=d, l_min=1, l_max=90, seed=3 + d, spare=4)
+    S, H = 5, 3
+    mp = inp.block_table.shape[1]
+    sentinel = -12345
+    ko = torch.full((S, H, mp * 16, d), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vo = torch.full((S, H, mp * 16, d), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    A.attn_gather_paged(cuda(inp.k_pool), cuda(inp.v_pool), cuda(inp.block_table), cuda(inp.seq_lens), ko, vo)
+    torch.cuda.synchronize()
+    kg = oracle.gather(inp.k_pool.view(torch.int16).numpy(), inp.block_table.numpy(), inp.seq_lens.numpy())
+    vg = oracle.gather(inp.v_pool.view(torch.int16).numpy(), inp.block_table.numpy(), inp.seq_lens.numpy())
+    kc, vc = ko.view(torch.int16).cpu().numpy(), vo.view(torch.int16).cpu().numpy()
+    for s in range(S):
+        L = int(inp.seq_lens[s])
+        assert np.array_equal(kc[s, :, :L], kg[s]) and np.array_equal(vc[s, :, :L], vg[s])
+        assert np.all(kc[s, :, L:] == sentinel) and np.all(vc[s, :, L:] == sentinel)
+
+
+def test_workload_4_full_size():
+    w = wl.WORKLOADS[4]
+    seed = wl.default_seed(4)
+    say(f"{w.name}: generating pool (seed {seed})")
+    inp = wl.paged_inputs(w.n_seq, w.H, w.d, w.l_min, w.l_max, seed=seed, page_size=w.page_size,
+                          spare=w.spare_pages)
+    say(f"{w.name}: {int(inp.seq_lens.sum())} tokens, pool {tuple(inp.k_pool.shape)}")
+    o, lse = _decode(inp, w.scale, True)
+    o_direct, _ = _decode(inp, w.scale, False)
+    assert torch.isfinite(o).all()
+    seqs = [0, 1, 17, 31, 40, 63]
+    ref, ref_lse = _oracle_decode(inp, w.scale, seqs)
+    err = check_close(to_np(o)[seqs], ref, True, what=w.name)
+    check_close(to_np(o_direct)[seqs], ref, True, what=w.name + " (one pass)")
+    assert np.max(np.abs(to_np(lse)[seqs] - ref_lse)) <= 1e-3
+    say(f"{w.name}: sampled max abs err {err:.3g}")
+
+    # bit-exact gather of every sequence against the oracle's gather
+    say(f"{w.name}: gather")
+    mp = inp.block_table.shape[1]
+    ko = torch.empty((w.n_seq, w.H, mp * 16, w.d), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty_like(ko)
+    A.attn_gather_paged(cuda(inp.k_pool), cuda(inp.v_pool), cuda(inp.block_table), cuda(inp.seq_lens), ko, vo)
+    torch.cuda.synchronize()
+    kpool = inp.k_pool.view(torch.int16).numpy()
+    vpool = inp.v_pool.view(torch.int16).numpy()
+    bt, lens = inp.block_table.numpy(), inp.seq_lens.numpy()
+    for s in range(w.n_seq):
+        L = int(lens[s])
+        kg = oracle.gather(kpool, bt[s:s + 1], lens[s:s + 1])[0]
+        vg = oracle.gather(vpool, bt[s:s + 1], lens[s:s + 1])[0]
+        assert np.array_equal(ko[s, :, :L].view(torch.int16).cpu().numpy(), kg), s
+        assert np.array_equal(vo[s, :, :L].view(torch.int16).cpu().numpy(), vg), s

@@ -1,0 +1,180 @@
+"""ctypes binding of libattn.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls (see
+include/attn.h). Tensors are torch tensors on the GPU; their data pointers and
+the current HIP stream are passed through unchanged. A non-OK status raises
+ValueError (ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE) or
+RuntimeError (ATTN_ERR_LAUNCH). There is no fallback: if the library is not
+built, loading fails loudly.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_LAUNCH = range(5)
+ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = range(3)
+MASKS = {"none": 0, "causal": 1, "sliding": 2}
+
+# symbol -> (restype, argtypes)
+_c_int, _c_float, _p, _size = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_PROTOS = {
+    "attn_fwd": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                          _c_int, _c_int, _p, _p]),
+    "attn_fwd_fp8": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                              _c_int, _c_int, _p, _p]),
+    "attn_quant_fp8_block": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),
+    "attn_decode_paged_workspace_size": (_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "attn_decode_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_float, _p, _p, _size, _p]),
+    "attn_gather_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_int, _p]),
+    "attn_tile_class": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "attn_k_tile_range": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+    "attn_status_str": (ctypes.c_char_p, [_c_int]),
+    "attn_abi_version": (_c_int, []),
+}
+
+_lib = None
+
+
+def load():
+    """Load libattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m tiled_attention_amd.build` (there is no fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def symbols():
+    return list(_PROTOS)
+
+
+def _check(status):
+    if status == ATTN_OK:
+        return
+    msg = load().attn_status_str(status).decode()
+    if status in (ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE):
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            _require(t.is_cuda and t.is_contiguous(), "tensors must be contiguous GPU tensors")
+
+
+def attn_fwd(q, k, v, o, scale, mask="none", window=0, lse=None, stream=None):
+    """O = softmax(Q K^T * scale, mask) V for q, k, v, o of shape [B, H, N, d]."""
+    _dev(q, k, v, o, lse)
+    _require(q.dim() == 4 and q.shape == k.shape == v.shape == o.shape, "q, k, v, o must be [B, H, N, d]")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    B, H, N, d = q.shape
+    _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, _dtype_code(q), _dtype_code(o),
+                           float(scale), MASKS[mask], int(window), _ptr(lse), _stream(stream)))
+    return o
+
+
+def attn_fwd_fp8(q8, q_scale, k8, k_scale, v, o, scale, mask="none", window=0, qk_block=128, lse=None,
+                 stream=None):
+    """fp8 block-scaled Q, K (uint8 E4M3FN codes + fp32 block scales), bf16 V and O."""
+    _dev(q8, q_scale, k8, k_scale, v, o, lse)
+    _require(q8.dim() == 4 and q8.shape == k8.shape == v.shape == o.shape, "shapes must be [B, H, N, d]")
+    B, H, N, d = q8.shape
+    _check(load().attn_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), _ptr(o),
+                               B, H, N, d, int(qk_block), float(scale), MASKS[mask], int(window), _ptr(lse),
+                               _stream(stream)))
+    return o
+
+
+def attn_quant_fp8_block(x, codes, scales, block=128, stream=None):
+    """Per-block E4M3FN quantisation of x [B, H, N, d] fp32 into codes (uint8) and scales (fp32)."""
+    _dev(x, codes, scales)
+    B, H, N, d = x.shape
+    _check(load().attn_quant_fp8_block(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, int(block),
+                                       _stream(stream)))
+    return codes, scales
+
+
+def attn_decode_paged_workspace_size(S, H, d, max_pages, page_size=16):
+    return int(load().attn_decode_paged_workspace_size(S, H, d, max_pages, page_size))
+
+
+def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, scale, workspace=None, lse=None,
+                      stream=None):
+    """Single-token decode over a paged KV pool; workspace None -> one pass per (sequence, head)."""
+    _dev(q, k_pool, v_pool, block_table, seq_lens, o, workspace, lse)
+    S, H, d = q.shape
+    num_pages, _, page_size, _ = k_pool.shape
+    max_pages = block_table.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().attn_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                                    _ptr(o), S, H, d, page_size, max_pages, num_pages, float(scale), _ptr(lse),
+                                    _ptr(workspace), ws_bytes, _stream(stream)))
+    return o
+
+
+def attn_gather_paged(k_pool, v_pool, block_table, seq_lens, k_out, v_out, stream=None):
+    """Dense copies k_out/v_out [S, H, max_pages*page, d] of each sequence's pages."""
+    _dev(k_pool, v_pool, block_table, seq_lens, k_out, v_out)
+    num_pages, H, page_size, d = k_pool.shape
+    S, max_pages = block_table.shape
+    _check(load().attn_gather_paged(_ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), _ptr(k_out),
+                                    _ptr(v_out), S, H, d, page_size, max_pages, num_pages,
+                                    _dtype_code(k_pool), _stream(stream)))
+    return k_out, v_out
+
+
+def attn_tile_class(mask, window, N, m0, m1, n0, n1):
+    return int(load().attn_tile_class(MASKS[mask], window, N, m0, m1, n0, n1))
+
+
+def attn_k_tile_range(mask, window, N, m0, m1, bn):
+    lo, hi = _c_int(), _c_int()
+    _check(load().attn_k_tile_range(MASKS[mask], window, N, m0, m1, bn, ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
+def attn_status_str(status):
+    return load().attn_status_str(status).decode()
+
+
+def attn_abi_version():
+    return int(load().attn_abi_version())

@@ -1,0 +1,208 @@
+// C ABI of libattn.so: argument validation and dispatch to the gfx950 kernels.
+// Every check runs on the host before anything is enqueued, so a non-OK
+// status means no device work was issued.
+#include "attn.h"
+
+#include <stdint.h>
+
+#include "attn_common.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_mask(int mask, int window) {
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_SLIDING) return false;
+  if (mask == ATTN_MASK_SLIDING && window < 1) return false;
+  return true;
+}
+
+// Shared size checks: B, H, N >= 1; d > 0; B*H*N fits in 31 bits.
+attn_status check_dims(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if ((long long)B * H * N >= (1LL << 31)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                     attn_dtype in_dtype, attn_dtype out_dtype, float scale, attn_mask mask, int window,
+                     float* lse, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
+  if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (in_dtype != ATTN_F32 && in_dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (!valid_mask(mask, window)) return ATTN_ERR_INVALID_ARG;
+  if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_dims(B, H, N, d);
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = B * H;
+  a.N = N;
+  a.d = d;
+  a.mask = mask;
+  a.window = mask == ATTN_MASK_SLIDING ? window : 0;
+  a.scale = scale;
+  a.in_f32 = in_dtype == ATTN_F32;
+  a.out_f32 = out_dtype == ATTN_F32;
+  a.fp8 = false;
+  return launched(attn::launch_fwd(a, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                         const void* v, void* o, int B, int H, int N, int d, int qk_block, float scale,
+                         attn_mask mask, int window, float* lse, void* stream) {
+  if (!q8 || !q_scale || !k8 || !k_scale || !v || !o) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (!valid_mask(mask, window)) return ATTN_ERR_INVALID_ARG;
+  if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
+  if (qk_block < 1) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_dims(B, H, N, d);
+  if (st != ATTN_OK) return st;
+  if (qk_block != 128) return ATTN_ERR_UNSUPPORTED;
+  attn::FwdArgs a{};
+  a.q = q8;
+  a.k = k8;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.BH = B * H;
+  a.N = N;
+  a.d = d;
+  a.mask = mask;
+  a.window = mask == ATTN_MASK_SLIDING ? window : 0;
+  a.scale = scale;
+  a.in_f32 = false;
+  a.out_f32 = false;
+  a.fp8 = true;
+  return launched(attn::launch_fwd(a, (hipStream_t)stream));
+}
+
+attn_status attn_quant_fp8_block(const float* x, uint8_t* codes, float* scales, int B, int H, int N, int d,
+                                 int block, void* stream) {
+  if (!x || !codes || !scales) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (block < 1) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_dims(B, H, N, d);
+  if (st != ATTN_OK) return st;
+  if (block != 128) return ATTN_ERR_UNSUPPORTED;
+  return launched(attn::launch_quant_fp8(x, codes, scales, B * H, N, d, (hipStream_t)stream));
+}
+
+size_t attn_decode_paged_workspace_size(int S, int H, int d, int max_pages, int page_size) {
+  if (S < 1 || H < 1 || max_pages < 1 || (d != 64 && d != 128) || page_size != 16) return 0;
+  return attn::decode_workspace_bytes(S, H, d, max_pages);
+}
+
+static attn_status check_paged(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, int S, int H, int d, int page_size, int max_pages,
+                               int num_pages) {
+  if (!k_pool || !v_pool || !block_table || !seq_lens) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)block_table & 3u) || ((uintptr_t)seq_lens & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (S < 1 || H < 1 || d < 1 || page_size < 1 || max_pages < 1 || num_pages < 1) return ATTN_ERR_INVALID_ARG;
+  if ((long long)S * max_pages >= (1LL << 31) || (long long)num_pages * H * page_size >= (1LL << 31))
+    return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                              const int32_t* seq_lens, void* o, int S, int H, int d, int page_size, int max_pages,
+                              int num_pages, float scale, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!q || !o) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
+  if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_paged(k_pool, v_pool, block_table, seq_lens, S, H, d, page_size, max_pages, num_pages);
+  if (st != ATTN_OK) return st;
+  if (workspace) {
+    if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+    if (workspace_bytes < attn::decode_workspace_bytes(S, H, d, max_pages)) return ATTN_ERR_WORKSPACE;
+  }
+  attn::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.S = S;
+  a.H = H;
+  a.d = d;
+  a.max_pages = max_pages;
+  a.scale = scale;
+  return launched(attn::launch_decode(a, (hipStream_t)stream));
+}
+
+attn_status attn_gather_paged(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                              const int32_t* seq_lens, void* k_out, void* v_out, int S, int H, int d,
+                              int page_size, int max_pages, int num_pages, attn_dtype dtype, void* stream) {
+  if (!k_out || !v_out) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_out) || !aligned16(v_out)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_paged(k_pool, v_pool, block_table, seq_lens, S, H, d, page_size, max_pages, num_pages);
+  if (st != ATTN_OK) return st;
+  if ((long long)S * H * max_pages * page_size >= (1LL << 31)) return ATTN_ERR_INVALID_ARG;
+  attn::GatherArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.S = S;
+  a.H = H;
+  a.d = d;
+  a.max_pages = max_pages;
+  a.elem_bytes = dtype == ATTN_F32 ? 4 : 2;
+  return launched(attn::launch_gather(a, (hipStream_t)stream));
+}
+
+int attn_tile_class(attn_mask mask, int window, int N, int m0, int m1, int n0, int n1) {
+  if (!valid_mask(mask, window) || N < 1 || m0 < 0 || n0 < 0 || m1 < m0 || n1 < n0) return -1;
+  return attn::tile_class(mask, mask == ATTN_MASK_SLIDING ? window : 0, N, m0, m1, n0, n1);
+}
+
+attn_status attn_k_tile_range(attn_mask mask, int window, int N, int m0, int m1, int bn, int* t_lo, int* t_hi) {
+  if (!t_lo || !t_hi || !valid_mask(mask, window) || N < 1 || bn < 1 || m0 < 0 || m1 < m0)
+    return ATTN_ERR_INVALID_ARG;
+  attn::k_tile_range(mask, mask == ATTN_MASK_SLIDING ? window : 0, N, m0, m1, bn, t_lo, t_hi);
+  return ATTN_OK;
+}
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: valid but not implemented";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace too small";
+    case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
+  }
+  return "unknown attn_status";
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

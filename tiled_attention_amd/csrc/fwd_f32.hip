@@ -1,0 +1,175 @@
+// Flash-attention forward with fp32 Q/K/V, computed in fp32 on the vector ALUs.
+//
+// Same tiled online-softmax method as the MFMA kernel ("Flash MSA Attention
+// Kernel Implementation Tutorial", "Understanding Flash MSA Core Mechanics"),
+// kept in full fp32 because gfx950 has no reduced-precision path that would
+// preserve fp32 inputs. A workgroup of 256 threads owns 128 query rows; two
+// lanes share a row (each holds half of q and of the accumulator), so the
+// running m and l of a row are computed redundantly in both lanes and never
+// leave registers. K/V tiles of 32 keys are staged in LDS and read as
+// broadcasts (all lanes of a half read the same address).
+#include <type_traits>
+
+#include "attn_common.h"
+#include "launch.h"
+
+namespace attn {
+
+hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t stream);
+
+namespace {
+
+constexpr int BMF = 128;
+constexpr int BNF = 32;
+constexpr int NTF = 256;
+
+struct ParamsF {
+  const float* q;
+  const float* k;
+  const float* v;
+  void* o;
+  float* lse;
+  int N, window, n_qtiles;
+  float scale_log2;
+};
+
+template <int D, int MASK, bool OUT_F32>
+__global__ __launch_bounds__(NTF) void fwd_f32_kernel(ParamsF p) {
+  constexpr int HALF = D / 2;
+  constexpr int PITCH = D + 4;  // floats; keeps 16-byte row starts off one bank
+  __shared__ __attribute__((aligned(16))) float ks[BNF * PITCH];
+  __shared__ __attribute__((aligned(16))) float vs[BNF * PITCH];
+
+  const int bh = blockIdx.y;
+  const int qt = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int row_in = tid >> 1;
+  const int half = tid & 1;
+  const int N = p.N;
+  const int m0 = qt * BMF;
+  const int m1 = min(m0 + BMF, N);
+  const int qrow = m0 + row_in;
+  const size_t head = (size_t)bh * N;
+  const long long wlen = effective_window(MASK, p.window, N);
+
+  float q[HALF];
+  float acc[HALF];
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    q[i] = qrow < N ? p.q[(head + qrow) * D + half * HALF + i] : 0.f;
+    acc[i] = 0.f;
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+
+  int t_lo, t_hi;
+  k_tile_range(MASK, p.window, N, m0, m1, BNF, &t_lo, &t_hi);
+  constexpr int CH = D / 4;  // float4 per row
+  for (int kt = t_lo; kt < t_hi; ++kt) {
+    const int n0 = kt * BNF;
+    for (int c = tid; c < BNF * CH; c += NTF) {
+      const int r = c / CH, col = c % CH;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      if (n0 + r < N) {
+        kv = *(const float4*)(p.k + (head + n0 + r) * D + 4 * col);
+        vv = *(const float4*)(p.v + (head + n0 + r) * D + 4 * col);
+      }
+      *(float4*)(ks + r * PITCH + 4 * col) = kv;
+      *(float4*)(vs + r * PITCH + 4 * col) = vv;
+    }
+    __syncthreads();
+    float s[BNF];
+#pragma unroll
+    for (int j = 0; j < BNF; ++j) {
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < HALF; i += 4) {
+        const float4 kk = *(const float4*)(ks + j * PITCH + half * HALF + i);
+        dot = __builtin_fmaf(q[i], kk.x, dot);
+        dot = __builtin_fmaf(q[i + 1], kk.y, dot);
+        dot = __builtin_fmaf(q[i + 2], kk.z, dot);
+        dot = __builtin_fmaf(q[i + 3], kk.w, dot);
+      }
+      dot += __shfl_xor(dot, 1);
+      const int key = n0 + j;
+      s[j] = (key < N && key_visible(MASK, wlen, qrow, key)) ? dot : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int j = 1; j < BNF; ++j) mx = fmaxf(mx, s[j]);
+    const float c = p.scale_log2;
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < BNF; ++j) {
+      s[j] = exp2f(__builtin_fmaf(s[j], c, -m_use));
+      psum += s[j];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < BNF; ++j) {
+#pragma unroll
+      for (int i = 0; i < HALF; i += 4) {
+        const float4 vv = *(const float4*)(vs + j * PITCH + half * HALF + i);
+        acc[i] = __builtin_fmaf(s[j], vv.x, acc[i]);
+        acc[i + 1] = __builtin_fmaf(s[j], vv.y, acc[i + 1]);
+        acc[i + 2] = __builtin_fmaf(s[j], vv.z, acc[i + 2]);
+        acc[i + 3] = __builtin_fmaf(s[j], vv.w, acc[i + 3]);
+      }
+    }
+    __syncthreads();
+  }
+  if (qrow < N) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+      const float x = acc[i] * inv;
+      if constexpr (OUT_F32)
+        ((float*)p.o)[(head + qrow) * D + half * HALF + i] = x;
+      else
+        ((__bf16*)p.o)[(head + qrow) * D + half * HALF + i] = (__bf16)x;
+    }
+    if (p.lse != nullptr && half == 0)
+      p.lse[head + qrow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool OUT_F32>
+hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
+  ParamsF p;
+  p.q = (const float*)a.q;
+  p.k = (const float*)a.k;
+  p.v = (const float*)a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.N = a.N;
+  p.window = a.window;
+  p.n_qtiles = (a.N + BMF - 1) / BMF;
+  p.scale_log2 = a.scale * kLog2e;
+  dim3 grid(p.n_qtiles, a.BH);
+  switch (a.mask) {
+    case MASK_NONE:
+      hipLaunchKernelGGL((fwd_f32_kernel<D, MASK_NONE, OUT_F32>), grid, dim3(NTF), 0, stream, p);
+      break;
+    case MASK_CAUSAL:
+      hipLaunchKernelGGL((fwd_f32_kernel<D, MASK_CAUSAL, OUT_F32>), grid, dim3(NTF), 0, stream, p);
+      break;
+    default:
+      hipLaunchKernelGGL((fwd_f32_kernel<D, MASK_SLIDING, OUT_F32>), grid, dim3(NTF), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  if (!a.in_f32) return launch_fwd_mfma(a, stream);
+  if (a.out_f32) return a.d == 64 ? launch_f32_d<64, true>(a, stream) : launch_f32_d<128, true>(a, stream);
+  return a.d == 64 ? launch_f32_d<64, false>(a, stream) : launch_f32_d<128, false>(a, stream);
+}
+
+}  // namespace attn

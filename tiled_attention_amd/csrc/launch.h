@@ -1,0 +1,56 @@
+// Internal launcher interface between the host API (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;        // [BH, N, d] bf16 / f32 / fp8 bytes
+  const void* k;
+  const void* v;        // bf16 (f32 for the f32 path)
+  void* o;
+  float* lse;           // nullable
+  const float* q_scale; // fp8 only: [BH, ceil(N/128)]
+  const float* k_scale;
+  int BH, N, d, mask, window;
+  float scale;
+  bool in_f32, out_f32, fp8;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  void* workspace;      // nullable
+  int S, H, d, max_pages;
+  float scale;
+};
+
+struct GatherArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* k_out;
+  void* v_out;
+  int S, H, d, max_pages, elem_bytes;
+};
+
+// Pages per split of the split-KV decode, and the resulting workspace size.
+constexpr int kDecodeSplitPages = 32;
+size_t decode_workspace_bytes(int S, int H, int d, int max_pages);
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_quant_fp8(const float* x, uint8_t* codes, float* scales, int BH, int N, int d,
+                            hipStream_t stream);
+
+}  // namespace attn
