@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the flash-attention forward path on one MI355X.
+
+A step is one attn_fwd call over the causal bf16 prefill workload
+(B=4, H=16, N=2048, d=64, fp32 accumulate, bf16 out) with inputs resident in
+HBM. `value` is algorithmic TFLOP/s over the K timed steps (wall clock,
+synchronised on both sides); the flop count is 4*d per visible (query, key)
+pair, so masked pairs the method skips are not counted. The JSON line also
+carries:
+  roofline     -- the attention kernel's average launch time from HIP events
+                  on its stream, as achieved TFLOP/s against the dense bf16
+                  MFMA peak, plus measured HBM traffic when the committed
+                  counter summary matches the current kernel source;
+  cpu_baseline -- the fp64 CPU oracle timed on a bounded sample of the same
+                  workload, on this host's cores;
+  workloads    -- the other four workloads (fp32 single head, sliding window,
+                  paged decode in GB/s, fp8 causal), each timed with HIP events.
+One GPU only: --gpus above 1 exits with a message.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2       # dense fp8 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector
+PEAK_HBM_GBS = 8000.0          # HBM3E
+METRIC = "attention fwd TFLOPS and % of MI355X MFMA peak; paged decode GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["tiled_attention_amd/csrc/fwd_mfma.hip", "tiled_attention_amd/csrc/attn_common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(mask, n, window):
+    if mask == "none":
+        return n * n
+    if mask == "causal" or window >= n:
+        return n * (n + 1) // 2
+    return window * (window + 1) // 2 + (n - window) * window
+
+
+class Dense:
+    """A dense/causal/sliding attn_fwd workload with device-resident inputs."""
+
+    def __init__(self, key, seed):
+        import torch
+        from tiled_attention_amd import _lib as A
+        from tiled_attention_amd import workloads as wl
+        self.w = w = wl.WORKLOADS[key]
+        self.seed = seed
+        q, k, v = wl.dense_inputs(w.B, w.H, w.N, w.d, seed=seed)
+        if w.dtype == "f32":
+            self.q, self.k, self.v = (torch.from_numpy(x).cuda() for x in (q, k, v))
+        else:
+            self.q, self.k, self.v = (wl.to_bf16(x).cuda() for x in (q, k, v))
+        self.o = torch.empty(self.q.shape, dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16,
+                             device="cuda")
+        self.flops = 4.0 * w.d * visible_pairs(w.mask, w.N, w.window) * w.B * w.H
+        lib = A.load()
+        dt = A.ATTN_F32 if w.dtype == "f32" else A.ATTN_BF16
+        odt = A.ATTN_F32 if w.out_dtype == "f32" else A.ATTN_BF16
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        args = (ctypes.c_void_p(self.q.data_ptr()), ctypes.c_void_p(self.k.data_ptr()),
+                ctypes.c_void_p(self.v.data_ptr()), ctypes.c_void_p(self.o.data_ptr()),
+                w.B, w.H, w.N, w.d, dt, odt, w.scale, A.MASKS[w.mask], w.window, None, stream)
+        fn = lib.attn_fwd
+
+        def step():
+            st = fn(*args)
+            if st != 0:
+                raise RuntimeError(A.attn_status_str(st))
+        self.step = step
+
+    def describe(self):
+        w = self.w
+        return {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N, "head_dim": w.d,
+                "mask": w.mask, "window": w.window or None, "in_dtype": w.dtype, "out_dtype": w.out_dtype,
+                "seed": self.seed}
+
+
+class Fp8:
+    def __init__(self, key, seed):
+        import torch
+        from tiled_attention_amd import _lib as A
+        from tiled_attention_amd import workloads as wl
+        self.w = w = wl.WORKLOADS[key]
+        self.seed = seed
+        q, k, v = wl.dense_inputs(w.B, w.H, w.N, w.d, seed=seed, outlier_p=w.outlier_p,
+                                  outlier_scale=w.outlier_scale)
+        nb = -(-w.N // 128)
+        self.q8 = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+        self.k8 = torch.empty_like(self.q8)
+        self.sq = torch.empty((w.B, w.H, nb), dtype=torch.float32, device="cuda")
+        self.sk = torch.empty_like(self.sq)
+        A.attn_quant_fp8_block(torch.from_numpy(q).cuda(), self.q8, self.sq)
+        A.attn_quant_fp8_block(torch.from_numpy(k).cuda(), self.k8, self.sk)
+        self.v = wl.to_bf16(v).cuda()
+        self.o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        self.flops = 4.0 * w.d * visible_pairs(w.mask, w.N, w.window) * w.B * w.H
+
+        def step():
+            A.attn_fwd_fp8(self.q8, self.sq, self.k8, self.sk, self.v, self.o, w.scale, w.mask)
+        self.step = step
+
+    def describe(self):
+        w = self.w
+        return {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N, "head_dim": w.d,
+                "mask": w.mask, "qk": "e4m3fn, fp32 scale per 128 rows", "v": "bf16", "seed": self.seed}
+
+
+class Paged:
+    def __init__(self, key, seed):
+        import torch
+        from tiled_attention_amd import _lib as A
+        from tiled_attention_amd import workloads as wl
+        self.w = w = wl.WORKLOADS[key]
+        self.seed = seed
+        inp = wl.paged_inputs(w.n_seq, w.H, w.d, w.l_min, w.l_max, seed=seed, page_size=w.page_size,
+                              spare=w.spare_pages)
+        self.q = inp.q.cuda()
+        self.kp, self.vp = inp.k_pool.cuda(), inp.v_pool.cuda()
+        self.bt, self.lens = inp.block_table.cuda(), inp.seq_lens.cuda()
+        self.o = torch.empty(self.q.shape, dtype=torch.bfloat16, device="cuda")
+        nbytes = A.attn_decode_paged_workspace_size(w.n_seq, w.H, w.d, self.bt.shape[1])
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        lens = inp.seq_lens.numpy().astype(int)
+        self.tokens = int(lens.sum())
+        pages = int(((lens + w.page_size - 1) // w.page_size).sum())
+        # compulsory bytes: every cached K and V element once, Q and O once, the page ids used, the lengths
+        self.bytes = (2.0 * self.tokens * w.H * w.d * 2 + 2.0 * w.n_seq * w.H * w.d * 2 + pages * 4 + w.n_seq * 4)
+        self.flops = 4.0 * w.d * self.tokens * w.H
+
+        def step():
+            A.attn_decode_paged(self.q, self.kp, self.vp, self.bt, self.lens, self.o, w.scale, workspace=self.ws)
+        self.step = step
+
+    def describe(self):
+        w = self.w
+        return {"workload": w.name, "sequences": w.n_seq, "heads": w.H, "head_dim": w.d,
+                "page_size": w.page_size, "kv_len": [w.l_min, w.l_max], "kv_tokens": self.tokens,
+                "seed": self.seed}
+
+
+def event_time_ms(step, reps, warmup=3):
+    """Average duration of one step from HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    times = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return sum(times) / len(times), times[len(times) // 2], times[0]
+
+
+def cpu_baseline(wk, budget_s=12.0):
+    """The oracle, untouched, on a bounded sample (whole heads) of the workload."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    from tiled_attention_amd import workloads as wl
+    w = wk.w
+    q = wk.q.float().cpu().numpy().reshape(-1, w.N, w.d).astype(np.float64)
+    k = wk.k.float().cpu().numpy().reshape(-1, w.N, w.d).astype(np.float64)
+    v = wk.v.float().cpu().numpy().reshape(-1, w.N, w.d).astype(np.float64)
+    heads, t0 = 0, time.perf_counter()
+    while True:          # whole heads, in order, wrapping around, until the budget is spent
+        h = heads % q.shape[0]
+        oracle.attention(q[h], k[h], v[h], w.scale, w.mask, w.window or None)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * visible_pairs(w.mask, w.N, w.window) * heads
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} head evaluations (heads of {w.name} in order, {q.shape[0]} per pass), "
+                      f"fp64, {dt:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def traffic_for(digest):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_digest") != digest:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--only-main", action="store_true", help="time only the causal prefill workload")
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="workload for --only-main runs (profiling); the JSON line always reports 2 otherwise")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the kernels shard by head or sequence with no exchange, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tiled_attention_amd import workloads as wl
+    from tiled_attention_amd import _lib as A
+    A.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    def make(key):
+        seed = args.seed if args.seed is not None else wl.default_seed(key)
+        w = wl.WORKLOADS[key]
+        return (Paged if w.kind == "paged" else Fp8 if w.kind == "fp8" else Dense)(key, seed)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copied {args.copy_calibration_mib} MiB three times (calibration)")
+        del src, dst
+
+    main_key = args.workload if args.only_main else 2
+    log(f"bench: preparing workload {main_key}")
+    wk = make(main_key)
+    for _ in range(args.warmup):
+        wk.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wk.step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    avg_ms, med_ms, min_ms = event_time_ms(wk.step, max(args.steps, 20))
+    log(f"bench: workload {main_key}: wall {ms_step:.4f} ms/step, kernel avg {avg_ms:.4f} ms")
+
+    if isinstance(wk, Paged):
+        value, unit = wk.bytes / (ms_step * 1e-3) / 1e9, "GB/s"
+        achieved, peak, runit, bound = wk.bytes / (avg_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    else:
+        value, unit = wk.flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+        achieved, runit = wk.flops / (avg_ms * 1e-3) / 1e12, "TFLOP/s"
+        if isinstance(wk, Fp8):
+            peak, bound = PEAK_FP8_TFLOPS, "mfma"
+        elif wk.w.dtype == "f32":
+            peak, bound = PEAK_FP32_VALU_TFLOPS, "alu"
+        else:
+            peak, bound = PEAK_BF16_TFLOPS, "mfma"
+    digest = kernel_source_digest()
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(digest) if main_key == 2 else None,
+            "kernel": "fwd_mfma_kernel<64, causal, bf16>" if main_key == 2 else f"workload {main_key}",
+            "kernel_avg_ms": round(avg_ms, 5), "kernel_median_ms": round(med_ms, 5), "kernel_min_ms": round(min_ms, 5),
+            "algorithmic_flops_per_launch": wk.flops, "kernel_source_digest": digest}
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if not isinstance(wk, Fp8) else "fp8e4m3+bf16",
+        "data": "synthetic", "config": wk.describe(), "roofline": roof,
+    }
+
+    if not args.only_main:
+        others = {}
+        for key, reps in ((1, 200), (3, 20), (4, 20), (5, 20)):
+            log(f"bench: workload {key}")
+            o = make(key)
+            avg, med, mn = event_time_ms(o.step, reps)
+            entry = {"config": o.describe(), "ms_avg": round(avg, 5), "ms_median": round(med, 5),
+                     "ms_min": round(mn, 5)}
+            if isinstance(o, Paged):
+                gbs = o.bytes / (avg * 1e-3) / 1e9
+                entry.update({"value": round(gbs, 1), "unit": "GB/s", "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                              "algorithmic_bytes": o.bytes})
+            else:
+                tf = o.flops / (avg * 1e-3) / 1e12
+                entry.update({"value": round(tf, 2), "unit": "TFLOP/s", "algorithmic_flops": o.flops})
+                if isinstance(o, Fp8):
+                    half = o.flops / 2
+                    blended_s = half / (PEAK_FP8_TFLOPS * 1e12) + half / (PEAK_BF16_TFLOPS * 1e12)
+                    entry.update({"frac_of_blended_peak": round(blended_s / (avg * 1e-3), 4),
+                                  "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                                  "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+                elif o.w.dtype == "f32":
+                    entry["frac_of_fp32_valu_peak"] = round(tf / PEAK_FP32_VALU_TFLOPS, 6)
+                else:
+                    entry["frac_of_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+            others[o.w.name] = entry
+            del o
+            torch.cuda.empty_cache()
+        result["workloads"] = others
+
+    if not args.no_cpu_baseline and not isinstance(wk, (Paged, Fp8)):
+        log("bench: cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(wk)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

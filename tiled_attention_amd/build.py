@@ -25,6 +25,8 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
+    # MFMA accumulators stay in VGPRs: the softmax reads and rescales them
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -42,6 +42,8 @@ namespace {
 constexpr int BM = 128;      // query rows per workgroup
 constexpr int BN = 64;       // keys per K/V tile
 constexpr int NT = 256;      // threads per workgroup
+constexpr float kLazy = 8.f; // log2 headroom before the reference max moves
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for gfx9 raw buffers
 
 template <int D, bool FP8>
 struct Lds {
@@ -129,32 +131,40 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
     for (int t = 0; t < QK_STEPS; ++t) qf[t] = (QFrag){};
   }
 
+  // Complete the Q loads here: the wait counter is in-order, so a Q load still
+  // pending inside the loop would make every tile wait for its own prefetch.
+#pragma unroll
+  for (int t = 0; t < QK_STEPS; ++t) asm volatile("" ::"v"(qf[t]));
+
   int t_lo, t_hi;
   k_tile_range(MASK, p.window, N, m0, m1, BN, &t_lo, &t_hi);
   const long long wlen = effective_window(MASK, p.window, N);
   float qscale = 1.f;
   if constexpr (FP8) qscale = p.q_scale[bh * p.nsb + m0 / 128];
 
-  float m_run = -INFINITY;
+  float m_ref = -INFINITY;   // reference max (log2 units) the exponentials are taken against
   float l_run = 0.f;
   f32x16 oacc[DE];
 #pragma unroll
   for (int e = 0; e < DE; ++e) oacc[e] = (f32x16){};
 
+  // Buffer resources over this head's K and V rows: loads past row N return 0.
+  const __amdgpu_buffer_rsrc_t kres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, N * KROW, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, N * (2 * D), kBufferFlags);
   i32x4 kreg[KLOADS], vreg[VLOADS];
   auto gload = [&](int kt) {
     const int n0 = kt * BN;
 #pragma unroll
     for (int i = 0; i < KLOADS; ++i) {
       const int c = tid + i * NT, row = c / KCH, col = c % KCH;
-      kreg[i] = (n0 + row < N) ? *(const i32x4*)(kbase + (size_t)(n0 + row) * KROW + col * 16)
-                               : (i32x4){0, 0, 0, 0};
+      kreg[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, (n0 + row) * KROW + col * 16, 0, 0));
     }
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int c = tid + i * NT, row = c / VCH, col = c % VCH;
-      vreg[i] = (n0 + row < N) ? *(const i32x4*)(vbase + (size_t)(n0 + row) * (2 * D) + col * 16)
-                               : (i32x4){0, 0, 0, 0};
+      vreg[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (n0 + row) * (2 * D) + col * 16, 0, 0));
     }
   };
   auto lstore = [&](int buf) {
@@ -230,40 +240,52 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
           }
       }
 
-      // ---- online softmax (log2 domain)
+      // ---- online softmax (log2 domain). The reference max m_ref only moves
+      // when a row's max exceeds it by more than 2^kLazy: the exponentials
+      // then stay <= 2^kLazy and the final O = acc / l is unchanged, while
+      // the rescale of acc by 2^(m_old - m_new) is skipped on most tiles.
       float mx = s[0][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = half_swap_max(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(__builtin_fmaf(s[b][r], c, -m_use));
-          s[b][r] = e;
-          psum += e;
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
+      const float mt = half_swap_max(mx) * c;
+      const bool move = mt > m_ref + kLazy;
+      if (__any(move)) {
+        const float m_new = move ? mt : m_ref;
+        // 1 for rows that keep their reference (also while it is still -inf), 0 for a first move
+        const float alpha = move ? fast_exp2(m_ref - m_new) : 1.f;
+        l_run *= alpha;
 #pragma unroll
         for (int e = 0; e < DE; ++e)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha;
+        m_ref = m_new;
       }
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
-      // ---- P as the B operand: k-step q covers keys 16q..16q+15 of the tile
+      // ---- P = 2^(s*c - m) rounded to bf16, laid out as the B operand: k-step q
+      // covers keys 16q..16q+15 of the tile. l sums the rounded values, so O is
+      // an exact convex combination of the V rows P multiplies.
       bf16x8 pf[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pf[q][j] = (__bf16)s[q >> 1][8 * (q & 1) + j];
+        for (int j = 0; j < 8; ++j)
+          pf[q][j] = (__bf16)fast_exp2(__builtin_fmaf(s[q >> 1][8 * (q & 1) + j], c, -m_use));
+      {
+        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+        const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+        float psum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2 pr = {pf[q][2 * j], pf[q][2 * j + 1]};
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+          }
+        l_run += psum;
+      }
 
       // ---- O^T += V^T P^T
 #pragma unroll
@@ -305,7 +327,7 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
         }
       }
     if (p.lse != nullptr && hl == 0)
-      p.lse[head + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      p.lse[head + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
