@@ -21,16 +21,18 @@ enum TileClass { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2 };
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Window length that makes SLIDING behave as CAUSAL for positions < N.
-__host__ __device__ inline long long effective_window(int mask, int window, int N) {
-  return mask == MASK_SLIDING ? (long long)window : (long long)N + 1;
+// Window length in keys: SLIDING's window clamped to N + 1 (a longer window
+// sees the same keys), CAUSAL's is N + 1. All mask arithmetic then stays in
+// [-N, 2N] and fits in 32 bits.
+__host__ __device__ inline int effective_window(int mask, int window, int N) {
+  return (mask == MASK_SLIDING && window <= N) ? window : N + 1;
 }
 
 // Key j visible to query i (both < N)? NONE: always; CAUSAL: j <= i;
-// SLIDING: i - window < j <= i.
-__host__ __device__ inline bool key_visible(int mask, long long w, int i, int j) {
+// SLIDING: i - window < j <= i. w is effective_window().
+__host__ __device__ inline bool key_visible(int mask, int w, int i, int j) {
   if (mask == MASK_NONE) return true;
-  return j <= i && (long long)j > (long long)i - w;
+  return j <= i && j > i - w;
 }
 
 // Class of the tile (query rows [m0, m1)) x (keys [n0, n1)).
@@ -47,10 +49,10 @@ __host__ __device__ inline int tile_class(int mask, int window, int N, int m0, i
   const bool ragged = n1 > N;
   const int n_last = (ragged ? N : n1) - 1;
   if (mask == MASK_NONE) return ragged ? TILE_PARTIAL : TILE_FULL;
-  const long long w = effective_window(mask, window, N);
+  const int w = effective_window(mask, window, N);
   if (n0 > m1 - 1) return TILE_EMPTY;
-  if ((long long)n_last < (long long)m0 - w + 1) return TILE_EMPTY;
-  if (!ragged && n_last <= m0 && (long long)n0 > (long long)(m1 - 1) - w) return TILE_FULL;
+  if (n_last < m0 - w + 1) return TILE_EMPTY;
+  if (!ragged && n_last <= m0 && n0 > (m1 - 1) - w) return TILE_FULL;
   return TILE_PARTIAL;
 }
 
@@ -72,9 +74,9 @@ __host__ __device__ inline void k_tile_range(int mask, int window, int N, int m0
   }
   int h = (m1 - 1) / bn + 1;
   if (h > nt) h = nt;
-  long long first = mask == MASK_SLIDING ? (long long)m0 - window + 1 : 0;
+  int first = mask == MASK_SLIDING ? m0 - effective_window(mask, window, N) + 1 : 0;
   if (first < 0) first = 0;
-  *lo = (int)(first / bn);
+  *lo = first / bn;
   *hi = h;
 }
 

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(NTF) void fwd_f32_kernel(ParamsF p) {
   const int m1 = min(m0 + BMF, N);
   const int qrow = m0 + row_in;
   const size_t head = (size_t)bh * N;
-  const long long wlen = effective_window(MASK, p.window, N);
+  const int wlen = effective_window(MASK, p.window, N);
 
   float q[HALF];
   float acc[HALF];

@@ -6,57 +6,90 @@
 // past it; each tile updates a running row max m and row sum l, rescales the
 // accumulator by exp(m - m_new), adds P V, and O = acc / l is written once.
 // fp8 scores: "FlashAttention-3 ...", "FP8 Block Quantization" -- the product
-// of the two blocks' scales multiplies the fp8 dot products, folded here into
-// the exponent's scale factor.
+// of the two blocks' scales multiplies the fp8 dot products; it is folded
+// into the exponent's scale factor.
 //
-// Mapping onto CDNA4 (one workgroup = 4 waves = 128 query rows, 32 per wave):
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (or v_mfma_f32_32x32x64_f8f6f4):
-//    K is the A operand, read from LDS; Q is the B operand, held in VGPRs for
-//    the whole K loop. In the 32x32 result, lane l owns query row l%32 and 16
-//    of the 32 keys; the other 16 keys of that row sit in lane l^32. The row
-//    max and row sum therefore need one cross-half exchange
-//    (v_permlane32_swap) per tile, the rest is in-lane.
-//  * O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: the exponentials P (rounded to
-//    bf16) are already laid out as the B operand -- the k index of the MFMA
-//    is matched to the keys each lane holds -- and V^T is read from a
-//    row-major V tile with ds_read_b64_tr_b16 (16 lanes read a 4x16 block and
-//    each receives one column). The accumulator O^T has the same lane ->
-//    query-row ownership as S^T, so the exp(m - m_new) rescale is lane-local.
-//  * K/V tiles of 64 keys are double-buffered in LDS: tile j+1 is fetched
-//    from HBM into registers while tile j is consumed, then stored to the
-//    other LDS slot; one barrier per tile.
+// Mapping onto CDNA4 (a workgroup is 4 waves = 128 query rows, 32 per wave):
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x64_f8f6f4 for
+//    fp8): K is the A operand, read from LDS; Q is the B operand, held in
+//    VGPRs for the whole K loop. In the 32x32 result lane l owns query row
+//    l%32 and 16 of the 32 keys; the other 16 keys of that row are in lane
+//    l^32, so a row reduction needs one v_permlane32_swap.
+//  * O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: P (rounded to bf16) is
+//    already laid out as the B operand -- the MFMA's k index is matched to
+//    the keys each lane holds -- and V^T comes from the row-major V tile
+//    through ds_read_b64_tr_b16 (16 lanes read a 4x16 block, each receives a
+//    column). O^T has the same lane -> row ownership as S^T, so the rescale
+//    is lane-local.
+//  * K and V tiles (64 keys) stream through LDS rings (3 slots, or 2 for
+//    d = 128 bf16) filled by LDS DMA (buffer_load_dwordx4 ... lds) ahead of
+//    use; a buffer
+//    descriptor per tile makes rows past the end read as zeros. Rows are
+//    stored unpadded with the 16-byte chunks XOR-swizzled by row, so the
+//    16-byte K reads and the transposed V reads hit distinct banks.
+//  * Software pipeline: while the VALU computes the softmax of tile i, the
+//    matrix cores run S = K Q^T of tile i+1 and O += P V of tile i-1 (P V is
+//    one tile behind, so neither depends on the softmax in flight); on full
+//    tiles the 16 MFMAs are interleaved with the VALU work in one block.
+//  * Lazy rescale: P = 2^(S*c - m_ref) against a reference max that moves
+//    only when a row max exceeds it by more than 2^8, so the exponentials
+//    stay <= 2^8 and the rescale of acc by 2^(m_old - m_new) is skipped on
+//    almost every tile; O = acc / l does not depend on the reference used.
+//    l sums the bf16-rounded P (v_dot2_f32_bf16), the weights P V applies.
 //  * Per wave, each K tile is classified EMPTY / PARTIAL / FULL against the
-//    wave's 32 rows: EMPTY tiles are skipped, only PARTIAL tiles evaluate the
-//    mask, and the tile loop never visits tiles outside the mask's band
-//    ("Optimizing Triton kernels for custom attention patterns on H100",
-//    Pattern B, loop bounds and edge-only masking).
-//  * Causal: each workgroup takes Q tiles t and T-1-t so all workgroups carry
-//    equal work; workgroup ids are mapped so that a head's tiles share an XCD
-//    (and its L2).
+//    wave's 32 rows: EMPTY tiles skip the MFMA and softmax work, only PARTIAL
+//    tiles evaluate the mask, and the tile loop never visits tiles outside
+//    the mask's band ("Optimizing Triton kernels for custom attention
+//    patterns on H100", Pattern B: loop bounds and edge-only masking).
+//  * Causal: a workgroup takes Q tiles t and T-1-t so all carry equal work;
+//    workgroup ids are mapped so that a head's tiles share an XCD (its L2).
+#include <type_traits>
+
 #include "attn_common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
-constexpr int BM = 128;      // query rows per workgroup
-constexpr int BN = 64;       // keys per K/V tile
-constexpr int NT = 256;      // threads per workgroup
-constexpr float kLazy = 8.f; // log2 headroom before the reference max moves
-constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for gfx9 raw buffers
+constexpr int BM = 128;       // query rows per workgroup
+constexpr int BN = 64;        // keys per K/V tile
+constexpr int NW = 4;         // waves per workgroup
+constexpr int NT = 64 * NW;   // threads per workgroup
+constexpr float kLazy = 8.f;              // log2 headroom before the reference max moves
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 (gfx9 raw buffer)
 
 template <int D, bool FP8>
-struct Lds {
-  // K tile: bf16 rows padded by 16 B, or fp8 rows padded by 16 B; V tile:
-  // bf16 rows padded by 32 B. The paddings keep the 16-byte K reads of 16
-  // consecutive rows and the transposed V reads on distinct banks.
-  static constexpr int K_PITCH = FP8 ? D + 16 : (D + 8) * 2;  // bytes
-  static constexpr int V_PITCH = D + 16;                     // bf16 elements
-  static constexpr int K_BYTES = BN * K_PITCH;
-  static constexpr int V_BYTES = BN * V_PITCH * 2;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int TOTAL = 2 * STAGE;
+struct Cfg {
+  static constexpr int KROW = FP8 ? D : 2 * D;  // bytes per K row
+  static constexpr int VROW = 2 * D;            // bytes per V row
+  static constexpr int K_SLOT = BN * KROW;
+  static constexpr int V_SLOT = BN * VROW;
+  static constexpr int KLD = K_SLOT / (16 * NT);  // DMA loads per thread per K tile
+  static constexpr int VLD = V_SLOT / (16 * NT);
+  // LDS ring slots for K and for V: loads run NS-1 tiles ahead. Three slots
+  // when two workgroups still fit in a CU's 160 KB, else two.
+  static constexpr int NS = 3 * (K_SLOT + V_SLOT) <= 80 * 1024 ? 3 : 2;
+  static constexpr int LDS = NS * (K_SLOT + V_SLOT);
+  static constexpr int QK_STEPS = FP8 ? D / 64 : D / 16;
+  static constexpr int DE = D / 32;             // 32-row blocks of O^T
 };
+
+// 16-byte-chunk swizzles (chunk ^ swz(row)). The 64 banks span 256 bytes:
+// four 64-byte rows, two 128-byte rows or one 256-byte row.
+//  K (16-byte reads of one chunk by 16 consecutive rows): rows that share
+//    bank positions get distinct chunks.
+//  V (transposed reads: 4 consecutive rows x 32 bytes, two such groups side
+//    by side): the 32-byte windows of the rows land on distinct banks.
+template <int ROWB>
+__device__ __forceinline__ int swz_k(int row) {
+  static_assert(ROWB == 64 || ROWB == 128 || ROWB == 256, "row size");
+  return ROWB == 64 ? (row >> 2) & 3 : ROWB == 128 ? (row >> 1) & 7 : row & 15;
+}
+template <int ROWB>
+__device__ __forceinline__ int swz_v(int row) {
+  static_assert(ROWB == 128 || ROWB == 256, "row size");
+  return ROWB == 128 ? ((row >> 1) & 1) << 2 : (row & 3) << 2;
+}
 
 struct Params {
   const void* q;
@@ -83,20 +116,47 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Raw buffer descriptor over [base, base + bytes).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r = {(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, kBufferFlags};
+  r[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  r[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  r[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  return r;
+}
+
+// 16 bytes per lane from buffer offset voff to LDS at m0 + lane * 16. The
+// compiler does not see this load: its completion is waited for explicitly
+// (sync_tiles). The s_nop covers the SALU-writes-M0 -> LDS DMA hazard.
+__device__ __forceinline__ void dma16(uint32_t m0v, int voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// Wait until at most N of this wave's loads are outstanding, then barrier.
+// One asm statement with a memory clobber, so no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void sync_tiles() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 template <int D, int MASK, bool FP8, bool OUT_F32>
 __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* smem, int bh, int qt) {
-  using L = Lds<D, FP8>;
-  constexpr int QK_STEPS = FP8 ? D / 64 : D / 16;  // MFMA k-steps for S
-  constexpr int KCH = FP8 ? D / 16 : D / 8;         // 16-byte chunks per K row
-  constexpr int VCH = D / 8;                        // 16-byte chunks per V row
-  constexpr int KLOADS = BN * KCH / NT;
-  constexpr int VLOADS = BN * VCH / NT;
-  constexpr int KROW = FP8 ? D : 2 * D;             // bytes per K row in HBM
-  constexpr int DE = D / 32;                        // 32-wide d blocks of O
+  using C = Cfg<D, FP8>;
+  constexpr int KROW = C::KROW, VROW = C::VROW, QK_STEPS = C::QK_STEPS, DE = C::DE;
+  constexpr int KLD = C::KLD, VLD = C::VLD, L = KLD + VLD, NS = C::NS;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave logic scalar
   const int l32 = lane & 31;
   const int hl = lane >> 5;
   const int N = p.N;
@@ -104,10 +164,9 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
   const int m1 = min(m0 + BM, N);
   const int wrow0 = m0 + wave * 32;
   const int qrow = wrow0 + l32;
-
   const size_t head = (size_t)bh * N;
   const unsigned char* kbase = (const unsigned char*)p.k + head * KROW;
-  const unsigned char* vbase = (const unsigned char*)p.v + head * (2 * D);
+  const unsigned char* vbase = (const unsigned char*)p.v + head * VROW;
 
   // ---- Q fragments: lane (row l32, half hl) holds the k-slots of half hl.
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type QFrag;
@@ -117,8 +176,8 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
       const unsigned char* qp = (const unsigned char*)p.q + (head + qrow) * D + 32 * hl;
 #pragma unroll
       for (int t = 0; t < QK_STEPS; ++t) {
-        i32x4 a = *(const i32x4*)(qp + 64 * t);
-        i32x4 b = *(const i32x4*)(qp + 64 * t + 16);
+        const i32x4 a = *(const i32x4*)(qp + 64 * t);
+        const i32x4 b = *(const i32x4*)(qp + 64 * t + 16);
         qf[t] = (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
       }
     } else {
@@ -130,182 +189,240 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
 #pragma unroll
     for (int t = 0; t < QK_STEPS; ++t) qf[t] = (QFrag){};
   }
-
-  // Complete the Q loads here: the wait counter is in-order, so a Q load still
-  // pending inside the loop would make every tile wait for its own prefetch.
+  // The Q loads complete here: an outstanding one inside the loop would make
+  // the in-order wait counter stall on the K/V prefetch as well.
 #pragma unroll
   for (int t = 0; t < QK_STEPS; ++t) asm volatile("" ::"v"(qf[t]));
 
   int t_lo, t_hi;
   k_tile_range(MASK, p.window, N, m0, m1, BN, &t_lo, &t_hi);
-  const long long wlen = effective_window(MASK, p.window, N);
+  const int NK = t_hi - t_lo;
+  const int wlen = effective_window(MASK, p.window, N);
   float qscale = 1.f;
   if constexpr (FP8) qscale = p.q_scale[bh * p.nsb + m0 / 128];
 
-  float m_ref = -INFINITY;   // reference max (log2 units) the exponentials are taken against
+  // ---- per-lane offsets (loop invariant)
+  int kdma[KLD], vdma[VLD];
+#pragma unroll
+  for (int u = 0; u < KLD; ++u) {
+    const int off = (u * NW + wave) * 1024 + lane * 16;
+    const int row = off / KROW, ch = (off % KROW) / 16;
+    kdma[u] = row * KROW + 16 * (ch ^ swz_k<KROW>(row));
+  }
+#pragma unroll
+  for (int u = 0; u < VLD; ++u) {
+    const int off = (u * NW + wave) * 1024 + lane * 16;
+    const int row = off / VROW, ch = (off % VROW) / 16;
+    vdma[u] = row * VROW + 16 * (ch ^ swz_v<VROW>(row));
+  }
+  // K read of k-step t: row l32 (block b adds 32 rows, same swizzle), chunk of half hl
+  constexpr int KCH_STEP = FP8 ? 4 : 2;  // 16-byte chunks per k-step
+  int kread[QK_STEPS * (FP8 ? 2 : 1)];
+#pragma unroll
+  for (int t = 0; t < QK_STEPS; ++t) {
+    if constexpr (FP8) {
+      const int c0 = KCH_STEP * t + 2 * hl;
+      kread[2 * t] = l32 * KROW + 16 * (c0 ^ swz_k<KROW>(l32));
+      kread[2 * t + 1] = l32 * KROW + 16 * ((c0 + 1) ^ swz_k<KROW>(l32));
+    } else {
+      kread[t] = l32 * KROW + 16 * ((KCH_STEP * t + hl) ^ swz_k<KROW>(l32));
+    }
+  }
+  // transposed V read: 16-lane group g, row rr of 4, 8-byte column piece cc
+  const int g = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
+  const int sv = swz_v<VROW>(4 * hl + rr);   // same for rows +16q and +8
+  int vread[DE];
+#pragma unroll
+  for (int e = 0; e < DE; ++e)
+    vread[e] = (4 * hl + rr) * VROW + 16 * ((4 * e + 2 * (g & 1) + (cc >> 1)) ^ sv) + 8 * (cc & 1);
+
+  const uint32_t lds0 = lds_addr(smem);
+  auto kslot = [&](int i) { return smem + ((i + NS) % NS) * C::K_SLOT; };
+  auto vslot = [&](int i) { return smem + NS * C::K_SLOT + ((i + NS) % NS) * C::V_SLOT; };
+
+  // DMA of K tile i (local index) and V tile j into their ring slots; tiles
+  // outside [0, NK) get an empty descriptor and write zeros to a free slot.
+  auto issue_k = [&](int i) {
+    const int n0 = (t_lo + i) * BN;
+    const bool live = i >= 0 && i < NK;
+    const i32x4 rs = make_rsrc(kbase + (size_t)(live ? n0 : 0) * KROW, live ? (uint32_t)(N - n0) * KROW : 0u);
+    const uint32_t base = lds0 + (uint32_t)(((i + NS) % NS) * C::K_SLOT);
+#pragma unroll
+    for (int u = 0; u < KLD; ++u)
+      dma16(__builtin_amdgcn_readfirstlane(base + (u * NW + wave) * 1024), kdma[u], rs);
+  };
+  auto issue_v = [&](int i) {
+    const int n0 = (t_lo + i) * BN;
+    const bool live = i >= 0 && i < NK;
+    const i32x4 rs = make_rsrc(vbase + (size_t)(live ? n0 : 0) * VROW, live ? (uint32_t)(N - n0) * VROW : 0u);
+    const uint32_t base = lds0 + (uint32_t)(NS * C::K_SLOT + ((i + NS) % NS) * C::V_SLOT);
+#pragma unroll
+    for (int u = 0; u < VLD; ++u)
+      dma16(__builtin_amdgcn_readfirstlane(base + (u * NW + wave) * 1024), vdma[u], rs);
+  };
+
+  auto wave_class = [&](int i) {
+    const int n0 = (t_lo + i) * BN;
+    return tile_class(MASK, p.window, N, wrow0, wrow0 + 32, n0, n0 + BN);
+  };
+
+  // S^T for keys n0..n0+31 (s[0]) and n0+32..n0+63 (s[1]) of the tile in K slot of i
+  auto qk = [&](int i, f32x16 (&s)[2]) {
+    const unsigned char* ks = kslot(i);
+    s[0] = (f32x16){};
+    s[1] = (f32x16){};
+#pragma unroll
+    for (int t = 0; t < QK_STEPS; ++t) {
+      if constexpr (FP8) {
+        const i32x4 a0l = *(const i32x4*)(ks + kread[2 * t]);
+        const i32x4 a0h = *(const i32x4*)(ks + kread[2 * t + 1]);
+        const i32x4 a1l = *(const i32x4*)(ks + kread[2 * t] + 32 * KROW);
+        const i32x4 a1h = *(const i32x4*)(ks + kread[2 * t + 1] + 32 * KROW);
+        const i32x8 a0 = {a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]};
+        const i32x8 a1 = {a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]};
+        s[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qf[t], s[0], 0, 0, 0, 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qf[t], s[1], 0, 0, 0, 0, 0, 0);
+      } else {
+        const bf16x8 a0 = *(const bf16x8*)(ks + kread[t]);
+        const bf16x8 a1 = *(const bf16x8*)(ks + kread[t] + 32 * KROW);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[t], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[t], s[1], 0, 0, 0);
+      }
+    }
+  };
+
+  float m_ref = -INFINITY;  // reference max (log2 units) of the exponentials
   float l_run = 0.f;
   f32x16 oacc[DE];
 #pragma unroll
   for (int e = 0; e < DE; ++e) oacc[e] = (f32x16){};
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-  // Buffer resources over this head's K and V rows: loads past row N return 0.
-  const __amdgpu_buffer_rsrc_t kres =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, N * KROW, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vres =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, N * (2 * D), kBufferFlags);
-  i32x4 kreg[KLOADS], vreg[VLOADS];
-  auto gload = [&](int kt) {
-    const int n0 = kt * BN;
+  // P = 2^(s*c - m_use) rounded to bf16 as the B operand (k-step q covers keys
+  // 16q..16q+15 of the tile); returns the sum of the rounded values (four
+  // independent partial sums keep the dependency chains short).
+  auto exponentials = [&](const f32x16 (&s)[2], float c, float m_use, bf16x8 (&pf)[4]) {
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int c = tid + i * NT, row = c / KCH, col = c % KCH;
-      kreg[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, (n0 + row) * KROW + col * 16, 0, 0));
-    }
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int c = tid + i * NT, row = c / VCH, col = c % VCH;
-      vreg[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, (n0 + row) * (2 * D) + col * 16, 0, 0));
-    }
-  };
-  auto lstore = [&](int buf) {
-    unsigned char* ks = smem + buf * L::STAGE;
-    unsigned char* vs = ks + L::K_BYTES;
+      for (int j = 0; j < 8; ++j) pf[q][j] = (__bf16)fast_exp2(__builtin_fmaf(s[q >> 1][8 * (q & 1) + j], c, -m_use));
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int c = tid + i * NT, row = c / KCH, col = c % KCH;
-      *(i32x4*)(ks + row * L::K_PITCH + col * 16) = kreg[i];
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 pr = {pf[q][2 * j], pf[q][2 * j + 1]};
+        ps[j] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[j], false);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int c = tid + i * NT, row = c / VCH, col = c % VCH;
-      *(i32x4*)(vs + row * (2 * L::V_PITCH) + col * 16) = vreg[i];
-    }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
 
-  // lane roles in the transposed V read: 16-lane group g, row rr, 4-column chunk cc
-  const int g = lane >> 4;
-  const int rr = (lane >> 2) & 3;
-  const int cc = lane & 3;
-  const int v_lane_off = (4 * hl + rr) * L::V_PITCH + 16 * (g & 1) + 4 * cc;  // elements
+  auto tile_scale = [&](int i) {
+    float c = p.scale_log2;
+    if constexpr (FP8) c *= qscale * p.k_scale[bh * p.nsb + ((t_lo + i) * BN) / 128];
+    return c;
+  };
 
-  if (t_lo < t_hi) {
-    gload(t_lo);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int kt = t_lo; kt < t_hi; ++kt) {
-    const int buf = (kt - t_lo) & 1;
-    const bool more = kt + 1 < t_hi;
-    if (more) gload(kt + 1);
-    const int n0 = kt * BN;
-    const int cls = tile_class(MASK, p.window, N, wrow0, wrow0 + 32, n0, n0 + BN);
-    if (cls != TILE_EMPTY) {
-      const unsigned char* ks = smem + buf * L::STAGE;
-      const __bf16* vs = (const __bf16*)(ks + L::K_BYTES);
-
-      // ---- S^T for keys n0..n0+31 (s[0]) and n0+32..n0+63 (s[1])
-      f32x16 s[2] = {(f32x16){}, (f32x16){}};
+  // O^T += V^T P^T for the tile whose V sits in the slot of local index j
+  auto pv = [&](int j, const bf16x8 (&pf)[4]) {
+    const unsigned char* vs = vslot(j);
 #pragma unroll
-      for (int t = 0; t < QK_STEPS; ++t) {
-        if constexpr (FP8) {
-          const unsigned char* a0p = ks + l32 * L::K_PITCH + 64 * t + 32 * hl;
-          const unsigned char* a1p = a0p + 32 * L::K_PITCH;
-          i32x4 a0l = *(const i32x4*)a0p, a0h = *(const i32x4*)(a0p + 16);
-          i32x4 a1l = *(const i32x4*)a1p, a1h = *(const i32x4*)(a1p + 16);
-          i32x8 a0 = {a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]};
-          i32x8 a1 = {a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]};
-          s[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qf[t], s[0], 0, 0, 0, 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qf[t], s[1], 0, 0, 0, 0, 0, 0);
-        } else {
-          const unsigned char* a0p = ks + l32 * L::K_PITCH + (16 * t + 8 * hl) * 2;
-          bf16x8 a0 = *(const bf16x8*)a0p;
-          bf16x8 a1 = *(const bf16x8*)(a0p + 32 * L::K_PITCH);
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[t], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[t], s[1], 0, 0, 0);
-        }
-      }
-
-      float c = p.scale_log2;
-      if constexpr (FP8) c *= qscale * p.k_scale[bh * p.nsb + n0 / 128];
-
-      // ---- mask (edge tiles only): key of s[b][r] is n0 + 32b + 8(r/4) + 4hl + r%4
-      if (cls == TILE_PARTIAL) {
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = n0 + 32 * b + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (!(key < N && key_visible(MASK, wlen, qrow, key))) s[b][r] = -INFINITY;
-          }
-      }
-
-      // ---- online softmax (log2 domain). The reference max m_ref only moves
-      // when a row's max exceeds it by more than 2^kLazy: the exponentials
-      // then stay <= 2^kLazy and the final O = acc / l is unchanged, while
-      // the rescale of acc by 2^(m_old - m_new) is skipped on most tiles.
-      float mx = s[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      const float mt = half_swap_max(mx) * c;
-      const bool move = mt > m_ref + kLazy;
-      if (__any(move)) {
-        const float m_new = move ? mt : m_ref;
-        // 1 for rows that keep their reference (also while it is still -inf), 0 for a first move
-        const float alpha = move ? fast_exp2(m_ref - m_new) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int e = 0; e < DE; ++e)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha;
-        m_ref = m_new;
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-      // ---- P = 2^(s*c - m) rounded to bf16, laid out as the B operand: k-step q
-      // covers keys 16q..16q+15 of the tile. l sums the rounded values, so O is
-      // an exact convex combination of the V rows P multiplies.
-      bf16x8 pf[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          pf[q][j] = (__bf16)fast_exp2(__builtin_fmaf(s[q >> 1][8 * (q & 1) + j], c, -m_use));
-      {
-        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-        const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-        float psum = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x2 pr = {pf[q][2 * j], pf[q][2 * j + 1]};
-            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
-          }
-        l_run += psum;
-      }
-
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int e = 0; e < DE; ++e) {
-          const __bf16* vp = vs + v_lane_off + 16 * q * L::V_PITCH + 32 * e;
-          s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vp));
-          s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vp + 8 * L::V_PITCH));
-          s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[q],
-                                                            oacc[e], 0, 0, 0);
-        }
+      for (int e = 0; e < DE; ++e) {
+        const unsigned char* vp = vs + vread[e] + 16 * q * VROW;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 8 * VROW));
+        const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[q], oacc[e], 0, 0, 0);
       }
     }
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // One pipeline step at local tile i: S of tile i+1 and P V of tile i-1 on
+  // the matrix cores, the softmax of tile i on the VALU, interleaved in one
+  // block. sc holds S_i, sn receives S_{i+1}; pp holds P_{i-1}, pc receives
+  // P_i. The reference max moves only when a row max exceeds it by more than
+  // 2^kLazy; acc is rescaled after the block, once P_{i-1} V (taken against
+  // the old reference) has been added.
+  auto step = [&](int i, f32x16 (&sc)[2], f32x16 (&sn)[2], const bf16x8 (&pp)[4], bf16x8 (&pc)[4], int& cls) {
+    // {K_{i+1}, V_{i-1}} landed; every wave is done with K_i and V_{i-2}
+    sync_tiles<(NS - 2) * L>();
+    issue_k(i + NS);
+    issue_v(i + NS - 2);
+    const int cls_n = i + 1 < NK ? wave_class(i + 1) : TILE_EMPTY;
+    const float c = tile_scale(i);
+    if (cls != TILE_FULL) {
+      // key of sc[b][r] is n0 + 32b + 8(r/4) + 4hl + r%4 (an EMPTY tile masks everything)
+      const int n0 = (t_lo + i) * BN;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = n0 + 32 * b + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (!(cls == TILE_PARTIAL && key < N && key_visible(MASK, wlen, qrow, key))) sc[b][r] = -INFINITY;
+        }
+    }
+    float mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+    const float mt = half_swap_max(mx) * c;
+    const bool move = mt > m_ref + kLazy;
+    const float alpha = move ? fast_exp2(m_ref - mt) : 1.f;   // 0 on a first move from -inf
+    if (move) m_ref = mt;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+
+    if (i + 1 < NK) qk(i + 1, sn);
+    pv(i - 1, pp);
+    const float psum = exponentials(sc, c, m_use, pc);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+    }
+    if (__any(move)) {
+#pragma unroll
+      for (int e = 0; e < DE; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha;
+    }
+    l_run = l_run * alpha + psum;
+    cls = cls_n;
+  };
+
+  // ---- prologue: K_0, then batches {K_{x+NS}, V_{x+NS-2}} for x = 1-NS .. -1
+  issue_k(0);
+#pragma unroll
+  for (int x = 1 - NS; x < 0; ++x) {
+    issue_k(x + NS);
+    issue_v(x + NS - 2);
   }
+  sync_tiles<(NS - 1) * L>();
+  f32x16 sa[2], sb[2];
+  bf16x8 pa[4], pb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pb[q] = (bf16x8){};
+  int cls = NK > 0 ? wave_class(0) : TILE_EMPTY;
+  if (NK > 0) qk(0, sa);
+
+  int i = 0;
+  for (; i + 1 < NK; i += 2) {
+    step(i, sa, sb, pb, pa, cls);
+    step(i + 1, sb, sa, pa, pb, cls);
+  }
+  if (i < NK) {
+    step(i, sa, sb, pb, pa, cls);
+    // P V of the last tile (its V is in the oldest outstanding batch)
+    sync_tiles<(NS - 2) * L>();
+    pv(NK - 1, pa);
+  } else if (NK > 0) {
+    sync_tiles<(NS - 2) * L>();
+    pv(NK - 1, pb);
+  }
+  // drain the DMA tail before the LDS is reused
+  sync_tiles<0>();
 
   // ---- epilogue: O = acc / l, written once
   const float l_tot = half_swap_sum(l_run);
@@ -322,7 +439,7 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
           *(float4*)((float*)p.o + (head + qrow) * D + d0) = make_float4(x0, x1, x2, x3);
         } else {
           typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-          bf16x4 ov = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+          const bf16x4 ov = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
           *(bf16x4*)((__bf16*)p.o + (head + qrow) * D + d0) = ov;
         }
       }
@@ -333,7 +450,7 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
 
 template <int D, int MASK, bool FP8, bool OUT_F32>
 __global__ __launch_bounds__(NT) void fwd_mfma_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<D, FP8>::TOTAL];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8>::LDS];
   const int u = xcd_unit(blockIdx.x, gridDim.x);
   if (u >= p.units) return;
   const int bh = u / p.units_per_bh;
@@ -341,10 +458,7 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(Params p) {
   if (p.pair) {
     const int ta = w, tb = p.n_qtiles - 1 - w;
     process_qtile<D, MASK, FP8, OUT_F32>(p, smem, bh, tb);
-    if (ta != tb) {
-      __syncthreads();
-      process_qtile<D, MASK, FP8, OUT_F32>(p, smem, bh, ta);
-    }
+    if (ta != tb) process_qtile<D, MASK, FP8, OUT_F32>(p, smem, bh, ta);
   } else {
     process_qtile<D, MASK, FP8, OUT_F32>(p, smem, bh, p.n_qtiles - 1 - w);
   }
