@@ -116,6 +116,14 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b, c) in one v_max3_f32. Scores are finite or -inf (never NaN), so
+// the IEEE-mode canonicalisation the compiler adds around fmaxf is not needed.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -340,37 +348,55 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
     }
   };
 
+  // Rescale of acc decided by the previous step, applied before P V of the
+  // tile whose P used the new reference joins acc.
+  float alpha_pending = 1.f;
+  auto apply_pending = [&]() {
+    if (__any(alpha_pending != 1.f)) {
+#pragma unroll
+      for (int e = 0; e < DE; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha_pending;
+      alpha_pending = 1.f;
+    }
+  };
+
   // One pipeline step at local tile i: S of tile i+1 and P V of tile i-1 on
-  // the matrix cores, the softmax of tile i on the VALU, interleaved in one
+  // the matrix cores, the softmax of tile i on the VALU, in one branch-free
   // block. sc holds S_i, sn receives S_{i+1}; pp holds P_{i-1}, pc receives
   // P_i. The reference max moves only when a row max exceeds it by more than
-  // 2^kLazy; acc is rescaled after the block, once P_{i-1} V (taken against
-  // the old reference) has been added.
+  // 2^kLazy; l follows at once, acc at the start of the next step (it still
+  // receives P_{i-1} V, taken against the previous reference).
   auto step = [&](int i, f32x16 (&sc)[2], f32x16 (&sn)[2], const bf16x8 (&pp)[4], bf16x8 (&pc)[4], int& cls) {
     // {K_{i+1}, V_{i-1}} landed; every wave is done with K_i and V_{i-2}
     sync_tiles<(NS - 2) * L>();
     issue_k(i + NS);
     issue_v(i + NS - 2);
+    apply_pending();
     const int cls_n = i + 1 < NK ? wave_class(i + 1) : TILE_EMPTY;
     const float c = tile_scale(i);
     if (cls != TILE_FULL) {
       // key of sc[b][r] is n0 + 32b + 8(r/4) + 4hl + r%4 (an EMPTY tile masks everything)
       const int n0 = (t_lo + i) * BN;
+      const bool partial = cls == TILE_PARTIAL;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = n0 + 32 * b + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (!(cls == TILE_PARTIAL && key < N && key_visible(MASK, wlen, qrow, key))) sc[b][r] = -INFINITY;
+          const bool vis = partial & (key < N) & key_visible(MASK, wlen, qrow, key);
+          sc[b][r] = vis ? sc[b][r] : -INFINITY;
         }
     }
-    float mx = fmaxf(sc[0][0], sc[1][0]);
+    // row max over the lane's 32 scores: 16 three-input maxes (fmaxf would
+    // first canonicalise every MFMA result, doubling the count)
+    float mx = -INFINITY;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+    for (int r = 0; r < 16; ++r) mx = max3(mx, sc[0][r], sc[1][r]);
     const float mt = half_swap_max(mx) * c;
     const bool move = mt > m_ref + kLazy;
     const float alpha = move ? fast_exp2(m_ref - mt) : 1.f;   // 0 on a first move from -inf
-    if (move) m_ref = mt;
+    m_ref = move ? mt : m_ref;
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 
     if (i + 1 < NK) qk(i + 1, sn);
@@ -379,17 +405,16 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
-    }
-    if (__any(move)) {
-#pragma unroll
-      for (int e = 0; e < DE; ++e)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha;
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
     }
     l_run = l_run * alpha + psum;
+    alpha_pending = alpha;
     cls = cls_n;
+    // keep this step's results here: otherwise the exponentials sink to their
+    // use in the next step and no longer overlap this step's MFMAs
+#pragma unroll
+    for (int q = 0; q < 4; ++q) asm volatile("" ::"v"(pc[q]));
+    asm volatile("" ::"v"(l_run));
   };
 
   // ---- prologue: K_0, then batches {K_{x+NS}, V_{x+NS-2}} for x = 1-NS .. -1
@@ -416,9 +441,11 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
     step(i, sa, sb, pb, pa, cls);
     // P V of the last tile (its V is in the oldest outstanding batch)
     sync_tiles<(NS - 2) * L>();
+    apply_pending();
     pv(NK - 1, pa);
   } else if (NK > 0) {
     sync_tiles<(NS - 2) * L>();
+    apply_pending();
     pv(NK - 1, pb);
   }
   // drain the DMA tail before the LDS is reused
