@@ -390,22 +390,32 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
     }
     // row max over the lane's 32 scores: 16 three-input maxes (fmaxf would
     // first canonicalise every MFMA result, doubling the count)
-    float mx = -INFINITY;
+    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // four short chains
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = max3(mx, sc[0][r], sc[1][r]);
+    for (int r = 0; r < 16; ++r) mq[r & 3] = max3(mq[r & 3], sc[0][r], sc[1][r]);
+    const float mx = max3(mq[0], mq[1], fmaxf(mq[2], mq[3]));
     const float mt = half_swap_max(mx) * c;
     const bool move = mt > m_ref + kLazy;
     const float alpha = move ? fast_exp2(m_ref - mt) : 1.f;   // 0 on a first move from -inf
     m_ref = move ? mt : m_ref;
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 
-    if (i + 1 < NK) qk(i + 1, sn);
+    // unconditional, so the block has no branch: for i + 1 == NK the slot holds
+    // the zeros loaded for the tile past the end, and the result is unused
+    qk(i + 1, sn);
     pv(i - 1, pp);
     const float psum = exponentials(sc, c, m_use, pc);
+    // issue order: while the row-max chain runs, MFMAs with a few VALU each;
+    // then each remaining MFMA followed by a run of exponentials
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+    for (int k = 0; k < 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 12; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
     }
     l_run = l_run * alpha + psum;
     alpha_pending = alpha;
