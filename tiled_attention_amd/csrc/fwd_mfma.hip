@@ -72,6 +72,11 @@ struct Cfg {
   static constexpr int LDS = NS * (K_SLOT + V_SLOT);
   static constexpr int QK_STEPS = FP8 ? D / 64 : D / 16;
   static constexpr int DE = D / 32;             // 32-row blocks of O^T
+  // Occupancy the register allocation aims at (waves per SIMD). d = 64: two,
+  // although the LDS ring would admit three workgroups per CU, so that the
+  // scheduler may keep a step's LDS operand reads in flight together.
+  static constexpr int WAVES_MIN = D == 64 ? 2 : 1;
+  static constexpr int WAVES_MAX = D == 64 ? 2 : 2;
 };
 
 // 16-byte-chunk swizzles (chunk ^ swz(row)). The 64 banks span 256 bytes:
@@ -161,6 +166,9 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
   using C = Cfg<D, FP8>;
   constexpr int KROW = C::KROW, VROW = C::VROW, QK_STEPS = C::QK_STEPS, DE = C::DE;
   constexpr int KLD = C::KLD, VLD = C::VLD, L = KLD + VLD, NS = C::NS;
+  // per step: LDS reads (K: 2 x QK_STEPS x (fp8: 2); V: 2 x 4 x DE) and MFMAs
+  constexpr int kStepReads = 2 * QK_STEPS * (FP8 ? 2 : 1) + 8 * DE;
+  constexpr int kStepMfma = 2 * QK_STEPS + 4 * DE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -325,9 +333,11 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
 
+  // log2-domain score scale of local tile i (i == NK, the zero tile past the
+  // end, takes the last tile's: its scores are all masked anyway)
   auto tile_scale = [&](int i) {
     float c = p.scale_log2;
-    if constexpr (FP8) c *= qscale * p.k_scale[bh * p.nsb + ((t_lo + i) * BN) / 128];
+    if constexpr (FP8) c *= qscale * p.k_scale[bh * p.nsb + ((t_lo + min(i, NK - 1)) * BN) / 128];
     return c;
   };
 
@@ -348,83 +358,78 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
     }
   };
 
-  // Rescale of acc decided by the previous step, applied before P V of the
-  // tile whose P used the new reference joins acc.
-  float alpha_pending = 1.f;
-  auto apply_pending = [&]() {
-    if (__any(alpha_pending != 1.f)) {
-#pragma unroll
-      for (int e = 0; e < DE; ++e)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha_pending;
-      alpha_pending = 1.f;
-    }
-  };
+  // The reference for tile i (m_use) and its factor alpha = 2^(m_prev - m_new)
+  // are decided as soon as S_i exists, at the end of step i-1; l takes alpha
+  // in step i, acc at the start of step i+1 (just before P_i V joins it, while
+  // P_{i-1} V, taken against the previous reference, is already in).
+  float m_use = 0.f, alpha_cur = 1.f, alpha_acc = 1.f;
 
-  // One pipeline step at local tile i: S of tile i+1 and P V of tile i-1 on
-  // the matrix cores, the softmax of tile i on the VALU, in one branch-free
-  // block. sc holds S_i, sn receives S_{i+1}; pp holds P_{i-1}, pc receives
-  // P_i. The reference max moves only when a row max exceeds it by more than
-  // 2^kLazy; l follows at once, acc at the start of the next step (it still
-  // receives P_{i-1} V, taken against the previous reference).
-  auto step = [&](int i, f32x16 (&sc)[2], f32x16 (&sn)[2], const bf16x8 (&pp)[4], bf16x8 (&pc)[4], int& cls) {
-    // {K_{i+1}, V_{i-1}} landed; every wave is done with K_i and V_{i-2}
-    sync_tiles<(NS - 2) * L>();
-    issue_k(i + NS);
-    issue_v(i + NS - 2);
-    apply_pending();
-    const int cls_n = i + 1 < NK ? wave_class(i + 1) : TILE_EMPTY;
-    const float c = tile_scale(i);
-    if (cls != TILE_FULL) {
-      // key of sc[b][r] is n0 + 32b + 8(r/4) + 4hl + r%4 (an EMPTY tile masks everything)
-      const int n0 = (t_lo + i) * BN;
-      const bool partial = cls == TILE_PARTIAL;
+  // mask (edge tiles), row max and reference update for the scores s of tile j
+  auto prepare = [&](int j, f32x16 (&s)[2], int cls_j) {
+    if (cls_j != TILE_FULL) {
+      // key of s[b][r] is n0 + 32b + 8(r/4) + 4hl + r%4 (an EMPTY tile masks everything)
+      const int n0 = (t_lo + j) * BN;
+      const bool partial = cls_j == TILE_PARTIAL;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = n0 + 32 * b + 8 * (r >> 2) + 4 * hl + (r & 3);
           const bool vis = partial & (key < N) & key_visible(MASK, wlen, qrow, key);
-          sc[b][r] = vis ? sc[b][r] : -INFINITY;
+          s[b][r] = vis ? s[b][r] : -INFINITY;
         }
     }
-    // row max over the lane's 32 scores: 16 three-input maxes (fmaxf would
-    // first canonicalise every MFMA result, doubling the count)
-    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // four short chains
+    // row max over the lane's 32 scores: three-input maxes in four chains
+    // (fmaxf would first canonicalise every MFMA result)
+    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mq[r & 3] = max3(mq[r & 3], sc[0][r], sc[1][r]);
-    const float mx = max3(mq[0], mq[1], fmaxf(mq[2], mq[3]));
-    const float mt = half_swap_max(mx) * c;
+    for (int r = 0; r < 16; ++r) mq[r & 3] = max3(mq[r & 3], s[0][r], s[1][r]);
+    const float mt = half_swap_max(max3(mq[0], mq[1], fmaxf(mq[2], mq[3]))) * tile_scale(j);
     const bool move = mt > m_ref + kLazy;
-    const float alpha = move ? fast_exp2(m_ref - mt) : 1.f;   // 0 on a first move from -inf
+    alpha_cur = move ? fast_exp2(m_ref - mt) : 1.f;   // 0 on a first move from -inf
     m_ref = move ? mt : m_ref;
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    m_use = m_ref == -INFINITY ? 0.f : m_ref;
+  };
 
+  // One pipeline step at local tile i: S of tile i+1 and P V of tile i-1 on
+  // the matrix cores, the exponentials of tile i on the VALU, in one
+  // branch-free block; then the next tile's mask/max. sc holds S_i (masked,
+  // reference decided), sn receives S_{i+1}; pp holds P_{i-1}, pc receives P_i.
+  auto step = [&](int i, f32x16 (&sc)[2], f32x16 (&sn)[2], const bf16x8 (&pp)[4], bf16x8 (&pc)[4], int& cls) {
+    // {K_{i+1}, V_{i-1}} landed; every wave is done with K_i and V_{i-2}
+    sync_tiles<(NS - 2) * L>();
+    issue_k(i + NS);
+    issue_v(i + NS - 2);
+    if (__any(alpha_acc != 1.f)) {
+#pragma unroll
+      for (int e = 0; e < DE; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha_acc;
+    }
+    const int cls_n = i + 1 < NK ? wave_class(i + 1) : TILE_EMPTY;
+    const float c = tile_scale(i);
     // unconditional, so the block has no branch: for i + 1 == NK the slot holds
-    // the zeros loaded for the tile past the end, and the result is unused
+    // the zeros loaded for the tile past the end (masked as EMPTY below)
     qk(i + 1, sn);
     pv(i - 1, pp);
     const float psum = exponentials(sc, c, m_use, pc);
-    // issue order: while the row-max chain runs, MFMAs with a few VALU each;
-    // then each remaining MFMA followed by a run of exponentials
+    // issue order: every LDS operand read of the step first, then each MFMA
+    // followed by a run of exponentials
+    __builtin_amdgcn_sched_group_barrier(0x100, kStepReads, 0);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kStepMfma; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
-#pragma unroll
-    for (int k = 0; k < 12; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-    }
-    l_run = l_run * alpha + psum;
-    alpha_pending = alpha;
-    cls = cls_n;
+    l_run = l_run * alpha_cur + psum;
+    alpha_acc = alpha_cur;
     // keep this step's results here: otherwise the exponentials sink to their
     // use in the next step and no longer overlap this step's MFMAs
 #pragma unroll
     for (int q = 0; q < 4; ++q) asm volatile("" ::"v"(pc[q]));
     asm volatile("" ::"v"(l_run));
+    prepare(i + 1, sn, cls_n);
+    cls = cls_n;
   };
 
   // ---- prologue: K_0, then batches {K_{x+NS}, V_{x+NS-2}} for x = 1-NS .. -1
@@ -440,23 +445,25 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
 #pragma unroll
   for (int q = 0; q < 4; ++q) pb[q] = (bf16x8){};
   int cls = NK > 0 ? wave_class(0) : TILE_EMPTY;
-  if (NK > 0) qk(0, sa);
+  if (NK > 0) {
+    qk(0, sa);
+    prepare(0, sa, cls);
+  }
 
   int i = 0;
   for (; i + 1 < NK; i += 2) {
     step(i, sa, sb, pb, pa, cls);
     step(i + 1, sb, sa, pa, pb, cls);
   }
-  if (i < NK) {
-    step(i, sa, sb, pb, pa, cls);
+  if (i < NK) step(i, sa, sb, pb, pa, cls);
+  if (NK > 0) {
     // P V of the last tile (its V is in the oldest outstanding batch)
     sync_tiles<(NS - 2) * L>();
-    apply_pending();
-    pv(NK - 1, pa);
-  } else if (NK > 0) {
-    sync_tiles<(NS - 2) * L>();
-    apply_pending();
-    pv(NK - 1, pb);
+#pragma unroll
+    for (int e = 0; e < DE; ++e)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha_acc;
+    pv(NK - 1, (NK & 1) ? pa : pb);
   }
   // drain the DMA tail before the LDS is reused
   sync_tiles<0>();
@@ -486,7 +493,8 @@ __device__ __forceinline__ void process_qtile(const Params& p, unsigned char* sm
 }
 
 template <int D, int MASK, bool FP8, bool OUT_F32>
-__global__ __launch_bounds__(NT) void fwd_mfma_kernel(Params p) {
+__global__ __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(Cfg<D, FP8>::WAVES_MIN, Cfg<D, FP8>::WAVES_MAX))) void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8>::LDS];
   const int u = xcd_unit(blockIdx.x, gridDim.x);
   if (u >= p.units) return;
