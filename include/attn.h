@@ -171,6 +171,13 @@ int attn_tile_class(attn_mask mask, int window, int N, int m0, int m1, int n0, i
 attn_status attn_k_tile_range(attn_mask mask, int window, int N, int m0, int m1, int bn,
                               int* t_lo, int* t_hi);
 
+/* Global K-tile index range [*f_lo, *f_hi) of the tiles of bn keys that are
+ * FULL for the rows [m0, m1) (every pair visible: the kernels skip the mask
+ * there). FULL tiles of a band mask are contiguous; an empty range is
+ * returned as *f_lo == *f_hi. */
+attn_status attn_full_tile_range(attn_mask mask, int window, int N, int m0, int m1, int bn,
+                                 int* f_lo, int* f_hi);
+
 const char* attn_status_str(attn_status s);
 int attn_abi_version(void);
 

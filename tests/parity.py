@@ -14,10 +14,11 @@ import torch
 
 ATOL = 1e-2
 FP8_REL_RMSE = 5e-2
-# The MFMA kernels normalise by l = sum of the bf16-rounded weights P~ (the
-# weights P V actually uses). Each weight carries a relative rounding error of
-# at most 2^-9, so log l moves by at most -log(1 - 2^-9) = 1.955e-3; the LSE
-# they return is held to that bound plus fp32 slack.
+# The MFMA kernels apply P rounded to bf16 in P V but normalise by l, the fp32
+# sum of the unrounded P, so their LSE = m + log l carries only fp32 rounding.
+# It is held to the bound that a normaliser of bf16-rounded weights would
+# need, -log(1 - 2^-9) = 1.955e-3 plus fp32 slack, which also covers the
+# kernels that sum the rounded weights.
 LSE_TOL_MFMA = 2.5e-3
 
 

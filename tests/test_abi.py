@@ -159,6 +159,22 @@ def test_tile_class_and_range_match_oracle_mask(mask, window):
                     assert _expected_class(vis, N, m0, m1, (hi - 1) * bn, hi * bn) != 0
 
 
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 1), ("sliding", 3),
+                                         ("sliding", 16), ("sliding", 40)])
+def test_full_tile_range_is_exactly_the_full_tiles(mask, window):
+    """The kernels' closed-form FULL range equals the set of tiles whose every pair is visible."""
+    for N in (1, 5, 17, 40, 64, 100):
+        vis = oracle.visible(mask, N, N, window if mask == "sliding" else None)
+        for bm in (1, 3, 8, 32):
+            for bn in (1, 4, 16, 64):
+                for m0 in range(0, N, bm):
+                    lo, hi = _lib.attn_full_tile_range(mask, window, N, m0, m0 + bm, bn)
+                    assert 0 <= lo <= hi
+                    for t in range(-(-N // bn)):
+                        full = _expected_class(vis, N, m0, m0 + bm, t * bn, t * bn + bn) == 2
+                        assert full == (lo <= t < hi), (N, bm, bn, m0, t, lo, hi)
+
+
 def test_tile_counts_at_workload_sizes():
     """Tile pairs visited per head at BM=128, BN=64 (the MFMA kernel's tiles)."""
     def pairs(mask, window, N):

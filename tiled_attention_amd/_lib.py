@@ -34,6 +34,8 @@ _PROTOS = {
     "attn_tile_class": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_k_tile_range": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+    "attn_full_tile_range": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                      ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "attn_status_str": (ctypes.c_char_p, [_c_int]),
     "attn_abi_version": (_c_int, []),
 }
@@ -169,6 +171,12 @@ def attn_tile_class(mask, window, N, m0, m1, n0, n1):
 def attn_k_tile_range(mask, window, N, m0, m1, bn):
     lo, hi = _c_int(), _c_int()
     _check(load().attn_k_tile_range(MASKS[mask], window, N, m0, m1, bn, ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
+def attn_full_tile_range(mask, window, N, m0, m1, bn):
+    lo, hi = _c_int(), _c_int()
+    _check(load().attn_full_tile_range(MASKS[mask], window, N, m0, m1, bn, ctypes.byref(lo), ctypes.byref(hi)))
     return lo.value, hi.value
 
 

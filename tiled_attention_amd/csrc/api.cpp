@@ -192,6 +192,14 @@ attn_status attn_k_tile_range(attn_mask mask, int window, int N, int m0, int m1,
   return ATTN_OK;
 }
 
+attn_status attn_full_tile_range(attn_mask mask, int window, int N, int m0, int m1, int bn, int* f_lo,
+                                 int* f_hi) {
+  if (!f_lo || !f_hi || !valid_mask(mask, window) || N < 1 || bn < 1 || m0 < 0 || m1 < m0)
+    return ATTN_ERR_INVALID_ARG;
+  attn::full_tile_range(mask, mask == ATTN_MASK_SLIDING ? window : 0, N, m0, m1, bn, f_lo, f_hi);
+  return ATTN_OK;
+}
+
 const char* attn_status_str(attn_status s) {
   switch (s) {
     case ATTN_OK: return "ATTN_OK";

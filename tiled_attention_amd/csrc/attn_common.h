@@ -80,6 +80,31 @@ __host__ __device__ inline void k_tile_range(int mask, int window, int N, int m0
   *hi = h;
 }
 
+// Global K-tile index range [lo, hi) of tiles of bn keys that are FULL (every
+// pair visible) for the rows [m0, m1): wholly inside [0, N), every key at or
+// before the first row (causal/sliding), and every key inside the last row's
+// window (sliding). A band mask's FULL tiles are contiguous.
+__host__ __device__ inline void full_tile_range(int mask, int window, int N, int m0, int m1, int bn, int* lo,
+                                                int* hi) {
+  if (m1 > N) m1 = N;
+  if (m0 >= m1) {
+    *lo = 0;
+    *hi = 0;
+    return;
+  }
+  int h = N / bn;
+  int l = 0;
+  if (mask != MASK_NONE) {
+    const int c = (m0 + 1) / bn;  // n1 - 1 <= m0
+    if (c < h) h = c;
+    const int first = m1 - effective_window(mask, window, N);  // n0 >= m1 - w
+    if (first > 0) l = (first + bn - 1) / bn;
+  }
+  if (l > h) l = h;
+  *lo = l;
+  *hi = h;
+}
+
 // Workgroup id -> work unit, so that consecutive units land on one XCD.
 // Workgroups are dealt to the 8 XCDs round-robin by id; unit u is given to
 // workgroup (u % per_xcd) * 8 + u / per_xcd, i.e. XCD u / per_xcd, so a run
