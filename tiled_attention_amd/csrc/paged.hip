@@ -43,165 +43,181 @@ struct DecParams {
   float scale_log2;
 };
 
-__device__ __forceinline__ float dpp_quad_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+// x plus the value of the lane given by a DPP pattern within its row of 16
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float dpp_quad_xor2(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-}
-
-// Reduce over the 16 lanes that share lane % 4 (xor 4, 8, 16, 32).
-__device__ __forceinline__ float key_lanes_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 4));
-  x = fmaxf(x, __shfl_xor(x, 8));
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-__device__ __forceinline__ float key_lanes_sum(float x) {
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
+// Sum over each group of G consecutive lanes (G = 8 or 16), left in every lane
+// of the group: xor 1, xor 2, then the half-row and row mirrors.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  x = dpp_add<0xB1>(x);    // quad_perm(1,0,3,2)
+  x = dpp_add<0x4E>(x);    // quad_perm(2,3,0,1)
+  x = dpp_add<0x141>(x);   // row_half_mirror
+  if constexpr (G == 16) x = dpp_add<0x140>(x);   // row_mirror
   return x;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// A lane's moves of the reference beyond which its exponentials could grow
+// past 2^16 trigger a rebase; below it P stays far inside fp32.
+constexpr float kDecodeHeadroom = 16.f;
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
-  constexpr int E = D / 4;        // head-dim elements per lane
-  constexpr int W = E / 2;        // packed bf16 pairs per lane
-  constexpr int LD = E / 8;       // 16-byte loads per lane per page
+  // A (page, head) slice is 16 keys x D bf16, contiguous. Load j of a lane
+  // reads 16 bytes at 1024 j + 16 lane: key j*KPJ + lane/LPK, dims
+  // 8 (lane % LPK) .. +7. Every load instruction reads 1 KB contiguously.
+  constexpr int SLICE = PAGE * D * 2;
+  constexpr int NJ = SLICE / 1024;   // loads per lane per page and tensor
+  constexpr int LPK = D / 8;         // lanes per key
+  constexpr int KPJ = 64 / LPK;      // keys per load
   const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int s = blockIdx.z;
   const int lane = threadIdx.x;
-  const int key = lane >> 2;
-  const int ch = lane & 3;
   const int H = p.H;
   const int len = p.lens[s];
   const int npages = (len + PAGE - 1) / PAGE;
   const int pg0 = split * p.split_pages;
   if (pg0 >= npages) return;
   const int pg1 = min(pg0 + p.split_pages, npages);
+  const int kq = lane / LPK;         // key within a load group
+  const int dq = lane % LPK;         // 8-dim block
 
-  uint32_t qw[W];
+  uint32_t qw[4];
   {
-    const uint4* qp = (const uint4*)(p.q + ((size_t)s * H + h) * D + ch * E);
-#pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      const uint4 t = qp[i];
-      qw[4 * i] = t.x;
-      qw[4 * i + 1] = t.y;
-      qw[4 * i + 2] = t.z;
-      qw[4 * i + 3] = t.w;
-    }
+    const u32x4 t = *(const u32x4*)(p.q + ((size_t)s * H + h) * D + 8 * dq);
+    qw[0] = t[0];
+    qw[1] = t[1];
+    qw[2] = t[2];
+    qw[3] = t[3];
   }
-  float acc[E];
+  float acc[8];
 #pragma unroll
-  for (int i = 0; i < E; ++i) acc[i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  float m_ref = -INFINITY, l_lane = 0.f;
   const float c = p.scale_log2;
   const int32_t* bt = p.bt + (size_t)s * p.max_pages;
-  const size_t lane_off = (size_t)key * D + ch * E;   // elements within a (page, head) slice
+  const char* kbase = (const char*)p.kp + (size_t)h * SLICE + 16 * lane;
+  const char* vbase = (const char*)p.vp + (size_t)h * SLICE + 16 * lane;
+  const size_t page_stride = (size_t)H * SLICE;
 
+  int pid_vec = 0, batch = pg0 - 64;
   for (int pg = pg0; pg < pg1; pg += 2) {
+    if (pg - batch == 64) {
+      // the next 64 page ids of the range, one per lane
+      batch = pg;
+      pid_vec = pg + lane < pg1 ? bt[pg + lane] : 0;
+    }
+    const int pid0 = __builtin_amdgcn_readlane(pid_vec, pg - batch);
     const bool two = pg + 1 < pg1;
-    const int pid0 = __builtin_amdgcn_readfirstlane(bt[pg]);
-    const int pid1 = two ? __builtin_amdgcn_readfirstlane(bt[pg + 1]) : pid0;
-    const uint4* k0 = (const uint4*)(p.kp + ((size_t)pid0 * H + h) * (PAGE * D) + lane_off);
-    const uint4* v0 = (const uint4*)(p.vp + ((size_t)pid0 * H + h) * (PAGE * D) + lane_off);
-    const uint4* k1 = (const uint4*)(p.kp + ((size_t)pid1 * H + h) * (PAGE * D) + lane_off);
-    const uint4* v1 = (const uint4*)(p.vp + ((size_t)pid1 * H + h) * (PAGE * D) + lane_off);
-    uint4 kr0[LD], kr1[LD], vr0[LD], vr1[LD];
+    // a missing second page reads the first again (its P is 0)
+    const int pid1 = two ? __builtin_amdgcn_readlane(pid_vec, pg + 1 - batch) : pid0;
+    u32x4 kr[2][NJ], vr[2][NJ];
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      kr0[i] = k0[i];
-      kr1[i] = k1[i];
+    for (int j = 0; j < NJ; ++j) {
+      kr[0][j] = __builtin_nontemporal_load((const u32x4*)(kbase + pid0 * page_stride + 1024 * j));
+      kr[1][j] = __builtin_nontemporal_load((const u32x4*)(kbase + pid1 * page_stride + 1024 * j));
     }
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      vr0[i] = v0[i];
-      vr1[i] = v1[i];
+    for (int j = 0; j < NJ; ++j) {
+      vr[0][j] = __builtin_nontemporal_load((const u32x4*)(vbase + pid0 * page_stride + 1024 * j));
+      vr[1][j] = __builtin_nontemporal_load((const u32x4*)(vbase + pid1 * page_stride + 1024 * j));
     }
-    // q . k over this lane's quarter of d, then over the 4 lanes of the key
-    float d0 = 0.f, d1 = 0.f;
+    // scores (log2 units) of the lane's keys; -inf past the sequence or the range
+    float sc[2][NJ];
+    bool any_over = m_ref == -INFINITY;
 #pragma unroll
-    for (int i = 0; i < LD; ++i) {
-      const uint32_t a0[4] = {kr0[i].x, kr0[i].y, kr0[i].z, kr0[i].w};
-      const uint32_t a1[4] = {kr1[i].x, kr1[i].y, kr1[i].z, kr1[i].w};
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-        d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[4 * i + j]),
-                                             __builtin_bit_cast(bf16x2, a0[j]), d0, false);
-        d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[4 * i + j]),
-                                             __builtin_bit_cast(bf16x2, a1[j]), d1, false);
+      for (int j = 0; j < NJ; ++j) {
+        // the words go through a scalar array: a bit cast of a vector element
+        // directly is lowered to one register for every index
+        const uint32_t kw[4] = {kr[u][j][0], kr[u][j][1], kr[u][j][2], kr[u][j][3]};
+        float d = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[w]), __builtin_bit_cast(bf16x2, kw[w]), d,
+                                              false);
+        d = group_sum<LPK>(d);
+        const int t = (pg + u) * PAGE + j * KPJ + kq;
+        const bool ok = (u == 0 || two) && t < len;
+        sc[u][j] = ok ? d * c : -INFINITY;
+        any_over |= sc[u][j] > m_ref + kDecodeHeadroom;
       }
+    if (__builtin_expect(__any(any_over), 0)) {
+      // slow path: the reference becomes the exact running max
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) mx = fmaxf(mx, sc[u][j]);
+#pragma unroll
+      for (int o = LPK; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_new == m_ref ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_lane *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
     }
-    d0 += dpp_quad_xor1(d0);
-    d1 += dpp_quad_xor1(d1);
-    d0 += dpp_quad_xor2(d0);
-    d1 += dpp_quad_xor2(d1);
-    const int t0 = pg * PAGE + key;
-    const bool ok0 = t0 < len;
-    const bool ok1 = two && (t0 + PAGE) < len;
-    const float s0 = ok0 ? d0 * c : -INFINITY;
-    const float s1 = ok1 ? d1 * c : -INFINITY;
-    const float mx = key_lanes_max(fmaxf(s0, s1));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    const float p0 = ok0 ? __builtin_amdgcn_exp2f(s0 - m_use) : 0.f;
-    const float p1 = ok1 ? __builtin_amdgcn_exp2f(s1 - m_use) : 0.f;
-    l_run = l_run * alpha + p0 + p1;
-    m_run = m_new;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    // Only a step holding the sequence's last page (or no second page) has
+    // keys past the end, whose rows may hold anything: their V words are
+    // replaced by zeros there, since 0 * NaN would poison acc.
+    const bool tail = !two || (pg + 2) * PAGE > len;
 #pragma unroll
-    for (int i = 0; i < E; ++i) acc[i] *= alpha;
-    if (ok0) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < LD; ++i) {
-        const uint32_t w[4] = {vr0[i].x, vr0[i].y, vr0[i].z, vr0[i].w};
+      for (int j = 0; j < NJ; ++j) {
+        const float pj = __builtin_amdgcn_exp2f(sc[u][j] - m_use);
+        l_lane += pj;
+        u32x4 vw = vr[u][j];
+        if (tail) {
+          const bool ok = sc[u][j] != -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[8 * i + 2 * j] = __builtin_fmaf(p0, bf16_lo(w[j]), acc[8 * i + 2 * j]);
-          acc[8 * i + 2 * j + 1] = __builtin_fmaf(p0, bf16_hi(w[j]), acc[8 * i + 2 * j + 1]);
+          for (int w = 0; w < 4; ++w) vw[w] = ok ? vw[w] : 0u;
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc[2 * w] = __builtin_fmaf(pj, bf16_lo(vw[w]), acc[2 * w]);
+          acc[2 * w + 1] = __builtin_fmaf(pj, bf16_hi(vw[w]), acc[2 * w + 1]);
         }
       }
-    }
-    if (ok1) {
-#pragma unroll
-      for (int i = 0; i < LD; ++i) {
-        const uint32_t w[4] = {vr1[i].x, vr1[i].y, vr1[i].z, vr1[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[8 * i + 2 * j] = __builtin_fmaf(p1, bf16_lo(w[j]), acc[8 * i + 2 * j]);
-          acc[8 * i + 2 * j + 1] = __builtin_fmaf(p1, bf16_hi(w[j]), acc[8 * i + 2 * j + 1]);
-        }
-      }
-    }
   }
-  // sum l and acc over the 16 keys
-  const float l_tot = key_lanes_sum(l_run);
+  // sum over the lanes holding the same 8 dims (different keys); l_lane counts
+  // each key once per group of LPK lanes, so l is summed the same way
 #pragma unroll
-  for (int i = 0; i < E; ++i) acc[i] = key_lanes_sum(acc[i]);
-  if (key != 0) return;   // lanes 0..3 hold the full row, a quarter of d each
+  for (int o = LPK; o < 64; o <<= 1) {
+    l_lane += __shfl_xor(l_lane, o);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o);
+  }
+  if (lane >= LPK) return;   // lane dq < LPK holds dims 8 dq .. +7
   const size_t sh = (size_t)s * H + h;
+  const float l_tot = l_lane;
   if (p.direct) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* op = p.o + sh * D + ch * E;
+    typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8v;
+    bf16x8v ov;
 #pragma unroll
-    for (int i = 0; i < E; ++i) op[i] = (__bf16)(acc[i] * inv);
-    if (p.lse != nullptr && ch == 0)
-      p.lse[sh] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(acc[i] * inv);
+    *(bf16x8v*)(p.o + sh * D + 8 * dq) = ov;
+    if (p.lse != nullptr && lane == 0)
+      p.lse[sh] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     const size_t slot = sh * p.max_splits + split;
-    float* ap = p.ws_acc + slot * D + ch * E;
-#pragma unroll
-    for (int i = 0; i < E; i += 4) *(float4*)(ap + i) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
-    if (ch == 0) *(float2*)(p.ws_ml + 2 * slot) = make_float2(m_run, l_tot);
+    float* ap = p.ws_acc + slot * D + 8 * dq;
+    *(float4*)ap = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *(float4*)(ap + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (lane == 0) *(float2*)(p.ws_ml + 2 * slot) = make_float2(m_ref, l_tot);
   }
 }
 
