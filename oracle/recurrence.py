@@ -39,7 +39,7 @@ def _rescale_factor(m_old, m_ref):
 
 
 def partial_state(q, k, v, scale, mask="none", window=None, bn=None, key_lo=0, key_hi=None,
-                  q_pos=None):
+                  q_pos=None, doc_offsets=None):
     """Run the recurrence for one head over keys [key_lo, key_hi) in tiles of bn.
 
     q: [n_q, d] with absolute query positions ``q_pos`` (default 0..n_q-1);
@@ -54,7 +54,7 @@ def partial_state(q, k, v, scale, mask="none", window=None, bn=None, key_lo=0, k
     key_hi = n_k if key_hi is None else key_hi
     bn = max(1, key_hi - key_lo) if bn is None else bn
     q_pos = np.arange(n_q) if q_pos is None else np.asarray(q_pos)
-    vis_all = visible(mask, n_q, n_k, window, q_pos=q_pos)
+    vis_all = visible(mask, n_q, n_k, window, q_pos=q_pos, doc_offsets=doc_offsets)
     m = np.full(n_q, -np.inf)
     l = np.zeros(n_q)
     acc = np.zeros((n_q, v.shape[1]))
@@ -78,7 +78,7 @@ def _finish(l, acc):
     return np.divide(acc, l[:, None], out=np.zeros_like(acc), where=live[:, None])
 
 
-def tiled_attention(q, k, v, scale, mask="none", window=None, bm=None, bn=None):
+def tiled_attention(q, k, v, scale, mask="none", window=None, bm=None, bn=None, doc_offsets=None):
     """Flash-style forward for one head: Q tiles of bm rows, K/V tiles of bn keys.
 
     Every K tile is visited (masked ones contribute nothing). Returns O [n_q, dv].
@@ -90,7 +90,7 @@ def tiled_attention(q, k, v, scale, mask="none", window=None, bm=None, bn=None):
     for m0 in range(0, n_q, bm):
         m1 = min(m0 + bm, n_q)
         _, l, acc = partial_state(q[m0:m1], k, v, scale, mask, window, bn,
-                                  q_pos=np.arange(m0, m1))
+                                  q_pos=np.arange(m0, m1), doc_offsets=doc_offsets)
         out[m0:m1] = _finish(l, acc)
     return out
 
@@ -109,7 +109,8 @@ def merge_partials(states):
     return m_star, l_star, acc_star
 
 
-def split_attention(q, k, v, scale, mask="none", window=None, bounds=(), bn=None, q_pos=None):
+def split_attention(q, k, v, scale, mask="none", window=None, bounds=(), bn=None, q_pos=None,
+                    doc_offsets=None):
     """Attention of one head computed as independent key ranges, then merged.
 
     ``bounds`` are interior split points of [0, n_k) (any order, duplicates
@@ -117,7 +118,7 @@ def split_attention(q, k, v, scale, mask="none", window=None, bounds=(), bn=None
     """
     n_k = np.asarray(k).shape[0]
     cuts = sorted(set([0, n_k] + [int(b) for b in bounds if 0 < b < n_k]))
-    states = [partial_state(q, k, v, scale, mask, window, bn, a, b, q_pos=q_pos)
+    states = [partial_state(q, k, v, scale, mask, window, bn, a, b, q_pos=q_pos, doc_offsets=doc_offsets)
               for a, b in zip(cuts[:-1], cuts[1:])]
     _, l, acc = merge_partials(states)
     return _finish(l, acc)
