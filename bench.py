@@ -13,8 +13,11 @@ carries:
                   counter summary matches the current kernel source;
   cpu_baseline -- the fp64 CPU oracle timed on a bounded sample of the same
                   workload, on this host's cores;
-  workloads    -- the other four workloads (fp32 single head, sliding window,
-                  paged decode in GB/s, fp8 causal), each timed with HIP events.
+  workloads    -- the other workloads (fp32 single head, sliding window,
+                  paged decode in GB/s, fp8 causal, documents, packed causal
+                  sequences, two-sided window, prefix-LM and the unmasked
+                  shape the document masks are compared with), each timed
+                  with HIP events.
 One GPU only: --gpus above 1 exits with a message.
 """
 
@@ -51,16 +54,28 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def visible_pairs(mask, n, window):
+def visible_pairs(mask, n, window, offs=None):
+    """Visible (query, key) pairs of one n x n head (closed forms per mask)."""
     if mask == "none":
         return n * n
-    if mask == "causal" or window >= n:
+    if mask == "causal" or (mask == "sliding" and window >= n):
         return n * (n + 1) // 2
-    return window * (window + 1) // 2 + (n - window) * window
+    if mask == "sliding":
+        return window * (window + 1) // 2 + (n - window) * window
+    if mask == "band":
+        w = min(window, n - 1)
+        return (2 * w + 1) * n - w * (w + 1)
+    if mask == "prefix_lm":
+        p = min(window, n)
+        return p * p + (n * (n + 1) - p * (p + 1)) // 2
+    lens = [int(b) - int(a) for a, b in zip(offs[:-1], offs[1:])]
+    if mask == "document":
+        return sum(x * x for x in lens)
+    return sum(x * (x + 1) // 2 for x in lens)     # document_causal
 
 
 class Dense:
-    """A dense/causal/sliding attn_fwd workload with device-resident inputs."""
+    """An attn_fwd workload (any mask) with device-resident inputs."""
 
     def __init__(self, key, seed):
         import torch
@@ -75,14 +90,18 @@ class Dense:
             self.q, self.k, self.v = (wl.to_bf16(x).cuda() for x in (q, k, v))
         self.o = torch.empty(self.q.shape, dtype=torch.float32 if w.out_dtype == "f32" else torch.bfloat16,
                              device="cuda")
-        self.flops = 4.0 * w.d * visible_pairs(w.mask, w.N, w.window) * w.B * w.H
+        self.offs = wl.document_offsets(w.N, w.l_min, w.l_max, seed) if w.mask in A.DOC_MASKS else None
+        self.doc = None if self.offs is None else torch.from_numpy(self.offs).cuda()
+        self.flops = 4.0 * w.d * visible_pairs(w.mask, w.N, w.window, self.offs) * w.B * w.H
         lib = A.load()
         dt = A.ATTN_F32 if w.dtype == "f32" else A.ATTN_BF16
         odt = A.ATTN_F32 if w.out_dtype == "f32" else A.ATTN_BF16
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         args = (ctypes.c_void_p(self.q.data_ptr()), ctypes.c_void_p(self.k.data_ptr()),
                 ctypes.c_void_p(self.v.data_ptr()), ctypes.c_void_p(self.o.data_ptr()),
-                w.B, w.H, w.N, w.d, dt, odt, w.scale, A.MASKS[w.mask], w.window, None, stream)
+                w.B, w.H, w.N, w.d, dt, odt, w.scale, A.MASKS[w.mask], w.window,
+                None if self.doc is None else ctypes.c_void_p(self.doc.data_ptr()),
+                0 if self.offs is None else len(self.offs) - 1, None, stream)
         fn = lib.attn_fwd
 
         def step():
@@ -93,9 +112,13 @@ class Dense:
 
     def describe(self):
         w = self.w
-        return {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N, "head_dim": w.d,
-                "mask": w.mask, "window": w.window or None, "in_dtype": w.dtype, "out_dtype": w.out_dtype,
-                "seed": self.seed}
+        d = {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.N, "head_dim": w.d,
+             "mask": w.mask, "window": w.window or None, "in_dtype": w.dtype, "out_dtype": w.out_dtype,
+             "seed": self.seed}
+        if self.offs is not None:
+            d["documents"] = len(self.offs) - 1
+            d["document_lengths"] = [w.l_min, w.l_max]
+        return d
 
 
 class Fp8:
@@ -192,12 +215,12 @@ def cpu_baseline(wk, budget_s=12.0):
     heads, t0 = 0, time.perf_counter()
     while True:          # whole heads, in order, wrapping around, until the budget is spent
         h = heads % q.shape[0]
-        oracle.attention(q[h], k[h], v[h], w.scale, w.mask, w.window or None)
+        oracle.attention(q[h], k[h], v[h], w.scale, w.mask, w.window or None, doc_offsets=wk.offs)
         heads += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.d * visible_pairs(w.mask, w.N, w.window) * heads
+    flops = 4.0 * w.d * visible_pairs(w.mask, w.N, w.window, wk.offs) * heads
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{heads} head evaluations (heads of {w.name} in order, {q.shape[0]} per pass), "
@@ -216,6 +239,11 @@ def traffic_for(digest):
     return t.get("bytes_per_launch")
 
 
+def wl_keys():
+    from tiled_attention_amd import workloads as wl
+    return wl.WORKLOADS.keys()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,7 +251,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--only-main", action="store_true", help="time only the causal prefill workload")
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(wl_keys()),
                     help="workload for --only-main runs (profiling); the JSON line always reports 2 otherwise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -300,7 +328,7 @@ def main():
 
     if not args.only_main:
         others = {}
-        for key, reps in ((1, 200), (3, 20), (4, 20), (5, 20)):
+        for key, reps in ((1, 200), (3, 20), (4, 20), (5, 20), (6, 20), (7, 20), (8, 10), (9, 20), (10, 20)):
             log(f"bench: workload {key}")
             o = make(key)
             avg, med, mn = event_time_ms(o.step, reps)
@@ -326,6 +354,13 @@ def main():
             others[o.w.name] = entry
             del o
             torch.cuda.empty_cache()
+        # Pattern A of the structured-mask page compares a document-masked
+        # kernel with plain attention on the same shape
+        dense = others.get(wl.WORKLOADS[10].name)
+        for key in (6, 7):
+            e = others.get(wl.WORKLOADS[key].name)
+            if dense and e:
+                e["ratio_to_unmasked_same_shape"] = round(e["value"] / dense["value"], 4)
         result["workloads"] = others
 
     if not args.no_cpu_baseline and not isinstance(wk, (Paged, Fp8)):

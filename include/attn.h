@@ -37,11 +37,11 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, misalignment, bad enum, window < 1 */
+  ATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, misalignment, bad enum, window out of range */
   ATTN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d = 96, page_size = 64) */
   ATTN_ERR_WORKSPACE = 3,    /* workspace smaller than the size query returns */
   ATTN_ERR_LAUNCH = 4        /* the HIP runtime reported a launch failure */
@@ -50,33 +50,65 @@ typedef enum {
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_FP8_E4M3 = 2 } attn_dtype;
 
 /* Visibility of key j to query i (square masks, positions 0..N-1):
- *   NONE    every key;
- *   CAUSAL  j <= i;
- *   SLIDING i - window < j <= i  (one-sided causal window of `window` keys,
- *           the query included). The window pattern is "Optimizing Triton
- *           kernels for custom attention patterns on H100", Pattern B. */
-typedef enum { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL = 1, ATTN_MASK_SLIDING = 2 } attn_mask;
+ *   NONE      every key;
+ *   CAUSAL    j <= i;
+ *   SLIDING   i - window < j <= i  (one-sided causal window of `window` keys,
+ *             the query included; window >= 1);
+ *   BAND      |i - j| <= window  (two-sided window of `window` neighbours on
+ *             each side; window >= 0);
+ *   PREFIX_LM j <= i or j < window  (the first `window` positions are a
+ *             prefix every query sees; window >= 0, 0 is CAUSAL);
+ *   DOCUMENT  i and j lie in the same document of doc_offsets (see below);
+ *   DOCUMENT_CAUSAL  same document and j <= i (packed variable-length
+ *             causal sequences).
+ * The window masks are "Optimizing Triton kernels for custom attention
+ * patterns on H100", Pattern B (which also names prefix-LM masks); the
+ * document masks are Pattern A of that page.
+ *
+ * Documents: doc_offsets is a device array of num_docs + 1 int32 with
+ * doc_offsets[0] = 0, doc_offsets[num_docs] = N, non-decreasing; document d
+ * holds positions [doc_offsets[d], doc_offsets[d+1]) (it may be empty), and
+ * every (batch, head) uses the same documents. A packed batch of sequences of
+ * different lengths is B = 1 with one document per sequence. The contents
+ * are the caller's contract and are not checked: other contents give
+ * unspecified results, but no access outside the arguments' buffers. For
+ * the other masks doc_offsets is ignored (may be NULL). */
+typedef enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_CAUSAL = 1,
+  ATTN_MASK_SLIDING = 2,
+  ATTN_MASK_BAND = 3,
+  ATTN_MASK_PREFIX_LM = 4,
+  ATTN_MASK_DOCUMENT = 5,
+  ATTN_MASK_DOCUMENT_CAUSAL = 6
+} attn_mask;
 
 /*
- * attn_fwd -- dense / causal / sliding-window prefill.
+ * attn_fwd -- prefill under any attn_mask (dense, causal, windows, prefix-LM,
+ * documents).
  *   q, k, v : [B, H, N, d], dtype in_dtype (ATTN_F32 or ATTN_BF16, all three alike).
  *   o       : [B, H, N, d], dtype out_dtype (ATTN_F32 or ATTN_BF16); every
  *             element is written (a row with no visible key, impossible for
  *             these masks, would be written as 0).
  *   scale   : multiplies Q K^T; the pages use 1/sqrt(d) (kernel listing in
  *             "Flash MSA ...", "Implementation Step-by-Step with Triton").
- *   mask, window : see attn_mask; window is ignored unless SLIDING (>= 1).
+ *   mask, window : see attn_mask; window is read by SLIDING, BAND and
+ *             PREFIX_LM only.
+ *   doc_offsets, num_docs : the documents of DOCUMENT / DOCUMENT_CAUSAL
+ *             (device int32 [num_docs + 1], num_docs >= 1); ignored otherwise.
  *   lse     : NULL, or [B, H, N] fp32 receiving log(sum_j exp(S_ij)) per row
  *             (natural log, scaled scores), -inf for a row with no visible key.
  * bf16 inputs run on bf16 MFMA with fp32 accumulation; fp32 inputs run in
  * fp32 throughout. The K/V loop skips tiles with no visible pair and applies
  * the mask only on tiles that straddle its edge ("Optimizing Triton kernels
- * ...", Pattern B).
+ * ...", Patterns A and B); document bounds are found on the device by a
+ * search of doc_offsets, once per query tile.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
                      int B, int H, int N, int d,
                      attn_dtype in_dtype, attn_dtype out_dtype,
                      float scale, attn_mask mask, int window,
+                     const int32_t* doc_offsets, int num_docs,
                      float* lse, void* stream);
 
 /*
@@ -89,13 +121,15 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
  *   S_ij = (sum_k q8_ik k8_jk) * q_scale[i/qk_block] * k_scale[j/qk_block] * scale,
  *   with the fp8 product accumulated in fp32; the rescale is folded into the
  *   exponent of the online softmax. P is rounded to bf16 for P V.
- *   qk_block must be 128. mask/window as in attn_fwd. lse: NULL or [B,H,N].
+ *   qk_block must be 128. mask, window, doc_offsets, num_docs as in
+ *   attn_fwd. lse: NULL or [B,H,N].
  */
 attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale,
                          const uint8_t* k8, const float* k_scale,
                          const void* v, void* o,
                          int B, int H, int N, int d, int qk_block,
                          float scale, attn_mask mask, int window,
+                         const int32_t* doc_offsets, int num_docs,
                          float* lse, void* stream);
 
 /*
@@ -157,26 +191,31 @@ attn_status attn_gather_paged(const void* k_pool, const void* v_pool,
                               attn_dtype dtype, void* stream);
 
 /*
- * Host-side tile planning (no device access). Tiles of query rows
- * [m0, m1) against keys [n0, n1) are EMPTY (0: no visible pair, never
- * loaded), PARTIAL (1: the mask is applied element by element) or FULL
- * (2: every pair visible, no mask work). Keys >= N do not exist, so a tile
- * reaching past N is at most PARTIAL; rows >= N are ignored.
- * Returns -1 on invalid arguments.
+ * Host-side tile planning (no device access). For every mask the keys
+ * visible to row i form one interval holding i whose ends never decrease
+ * with i, so a tile's class follows from the intervals of its first and last
+ * rows. Tiles of query rows [m0, m1) against keys [n0, n1) are EMPTY (0: no
+ * visible pair, never loaded), PARTIAL (1: the mask is applied element by
+ * element) or FULL (2: every pair visible, no mask work). Keys >= N do not
+ * exist, so a tile reaching past N is at most PARTIAL; rows >= N are ignored.
+ * doc_offsets here is a HOST array (num_docs + 1 entries, checked: 0 first,
+ * N last, non-decreasing) for the document masks and ignored otherwise.
+ * attn_tile_class returns -1 on invalid arguments.
  */
-int attn_tile_class(attn_mask mask, int window, int N, int m0, int m1, int n0, int n1);
+int attn_tile_class(attn_mask mask, int window, const int32_t* doc_offsets, int num_docs,
+                    int N, int m0, int m1, int n0, int n1);
 
 /* K-tile index range [*t_lo, *t_hi) (tiles of bn keys) that can hold a key
- * visible to some row of [m0, m1); tiles outside it are EMPTY. */
-attn_status attn_k_tile_range(attn_mask mask, int window, int N, int m0, int m1, int bn,
-                              int* t_lo, int* t_hi);
+ * visible to some row of [m0, m1); tiles outside it are EMPTY and none inside
+ * it is. An empty row range gives *t_lo == *t_hi == 0. */
+attn_status attn_k_tile_range(attn_mask mask, int window, const int32_t* doc_offsets, int num_docs,
+                              int N, int m0, int m1, int bn, int* t_lo, int* t_hi);
 
 /* Global K-tile index range [*f_lo, *f_hi) of the tiles of bn keys that are
  * FULL for the rows [m0, m1) (every pair visible: the kernels skip the mask
- * there). FULL tiles of a band mask are contiguous; an empty range is
- * returned as *f_lo == *f_hi. */
-attn_status attn_full_tile_range(attn_mask mask, int window, int N, int m0, int m1, int bn,
-                                 int* f_lo, int* f_hi);
+ * there). They are contiguous; an empty range is returned as *f_lo == *f_hi. */
+attn_status attn_full_tile_range(attn_mask mask, int window, const int32_t* doc_offsets, int num_docs,
+                                 int N, int m0, int m1, int bn, int* f_lo, int* f_hi);
 
 const char* attn_status_str(attn_status s);
 int attn_abi_version(void);

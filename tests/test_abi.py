@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     exported = set(re.findall(r"\bT (attn_\w+)", out))
     assert set(declared) <= exported
     assert set(_lib.symbols()) == set(declared)
-    assert _lib.attn_abi_version() == 1
+    assert _lib.attn_abi_version() == 2
 
 
 def test_status_strings():
@@ -47,11 +47,11 @@ def test_status_strings():
 
 def _fwd(**kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=1, N=8, d=64, ind=1, outd=1, scale=0.125,
-                mask=0, window=0, lse=None, stream=None)
+                mask=0, window=0, doc=None, nd=0, lse=None, stream=None)
     args.update(kw)
     return _lib.load().attn_fwd(args["q"], args["k"], args["v"], args["o"], args["B"], args["H"], args["N"],
                                 args["d"], args["ind"], args["outd"], args["scale"], args["mask"],
-                                args["window"], args["lse"], args["stream"])
+                                args["window"], args["doc"], args["nd"], args["lse"], args["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -65,8 +65,14 @@ def _fwd(**kw):
     (dict(d=256), _lib.ATTN_ERR_UNSUPPORTED),
     (dict(ind=2), _lib.ATTN_ERR_INVALID_ARG),
     (dict(outd=7), _lib.ATTN_ERR_INVALID_ARG),
-    (dict(mask=3), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(mask=7), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(mask=-1), _lib.ATTN_ERR_INVALID_ARG),
     (dict(mask=2, window=0), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(mask=3, window=-1), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(mask=4, window=-2), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(mask=5, doc=None, nd=2), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(mask=6, doc=FAKE, nd=0), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(mask=5, doc=FAKE + 2, nd=1), _lib.ATTN_ERR_INVALID_ARG),
     (dict(scale=float("nan")), _lib.ATTN_ERR_INVALID_ARG),
     (dict(B=1 << 16, H=1 << 16, N=1), _lib.ATTN_ERR_INVALID_ARG),
     (dict(lse=FAKE + 2), _lib.ATTN_ERR_INVALID_ARG),
@@ -77,7 +83,7 @@ def test_attn_fwd_rejects(kw, status):
 
 def test_attn_fwd_fp8_rejects():
     f = _lib.load().attn_fwd_fp8
-    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 128, 128, 0.1, 1, 0, None, None]
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 128, 128, 0.1, 1, 0, None, 0, None, None]
     bad = list(ok); bad[1] = None
     assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
     bad = list(ok); bad[10] = 64
@@ -87,6 +93,8 @@ def test_attn_fwd_fp8_rejects():
     bad = list(ok); bad[12] = 2; bad[13] = 0
     assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
     bad = list(ok); bad[2] = FAKE_MIS
+    assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
+    bad = list(ok); bad[12] = 5
     assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
 
 
@@ -135,44 +143,72 @@ def _expected_class(vis, N, m0, m1, n0, n1):
     return 1
 
 
-@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 1), ("sliding", 3),
-                                         ("sliding", 16), ("sliding", 40)])
+def _doc_sets(N):
+    """Document offsets exercised at length N: one document, single positions,
+    seeded random cuts with and without empty documents."""
+    rng = np.random.default_rng(N)
+    sets = [[0, N], list(range(N + 1))]
+    for k in (1, 3, max(1, N // 7)):
+        cuts = sorted(rng.integers(0, N + 1, size=k).tolist())
+        sets.append([0] + cuts + [N])
+        sets.append(sorted(set([0] + cuts + [N])))
+    return sets
+
+
+MASK_PLANS = [("none", 0), ("causal", 0), ("sliding", 1), ("sliding", 3), ("sliding", 16), ("sliding", 40),
+              ("band", 0), ("band", 2), ("band", 13), ("band", 70), ("prefix_lm", 0), ("prefix_lm", 7),
+              ("prefix_lm", 33), ("prefix_lm", 200), ("document", 0), ("document_causal", 0)]
+
+
+def _plans(mask, window, N):
+    """(oracle visibility, host offsets or None) for every offsets set of the mask."""
+    if mask in _lib.DOC_MASKS:
+        return [(oracle.visible(mask, N, N, doc_offsets=np.array(o)), o) for o in _doc_sets(N)]
+    return [(oracle.visible(mask, N, N, None if mask in ("none", "causal") else window), None)]
+
+
+@pytest.mark.parametrize("mask,window", MASK_PLANS)
 def test_tile_class_and_range_match_oracle_mask(mask, window):
     for N in (1, 5, 17, 40, 64):
-        vis = oracle.visible(mask, N, N, window if mask == "sliding" else None)
-        for bm in (1, 3, 8, 32):
-            for bn in (1, 4, 16, 64):
-                for m0 in range(0, N, bm):
-                    m1 = m0 + bm
-                    lo, hi = _lib.attn_k_tile_range(mask, window, N, m0, m1, bn)
-                    nt = -(-N // bn)
-                    assert 0 <= lo <= hi <= nt
-                    for t in range(nt):
-                        n0, n1 = t * bn, t * bn + bn
-                        want = _expected_class(vis, N, m0, m1, n0, n1)
-                        got = _lib.attn_tile_class(mask, window, N, m0, m1, n0, n1)
-                        assert got == want, (N, bm, bn, m0, t)
-                        if not lo <= t < hi:
-                            assert want == 0
-                    # the range is tight: its first and last tiles hold a visible pair
-                    assert _expected_class(vis, N, m0, m1, lo * bn, lo * bn + bn) != 0
-                    assert _expected_class(vis, N, m0, m1, (hi - 1) * bn, hi * bn) != 0
+        for vis, offs in _plans(mask, window, N):
+            for bm in (1, 3, 8, 32):
+                for bn in (1, 4, 16, 64):
+                    for m0 in range(0, N, bm):
+                        m1 = m0 + bm
+                        lo, hi = _lib.attn_k_tile_range(mask, window, N, m0, m1, bn, offs)
+                        nt = -(-N // bn)
+                        assert 0 <= lo <= hi <= nt
+                        for t in range(nt):
+                            n0, n1 = t * bn, t * bn + bn
+                            want = _expected_class(vis, N, m0, m1, n0, n1)
+                            got = _lib.attn_tile_class(mask, window, N, m0, m1, n0, n1, offs)
+                            assert got == want, (N, offs, bm, bn, m0, t)
+                            # outside the range every tile is EMPTY, inside none is
+                            assert (want != 0) == (lo <= t < hi), (N, offs, bm, bn, m0, t)
 
 
-@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("sliding", 1), ("sliding", 3),
-                                         ("sliding", 16), ("sliding", 40)])
+@pytest.mark.parametrize("mask,window", MASK_PLANS)
 def test_full_tile_range_is_exactly_the_full_tiles(mask, window):
-    """The kernels' closed-form FULL range equals the set of tiles whose every pair is visible."""
+    """The kernels' FULL range equals the set of tiles whose every pair is visible."""
     for N in (1, 5, 17, 40, 64, 100):
-        vis = oracle.visible(mask, N, N, window if mask == "sliding" else None)
-        for bm in (1, 3, 8, 32):
-            for bn in (1, 4, 16, 64):
-                for m0 in range(0, N, bm):
-                    lo, hi = _lib.attn_full_tile_range(mask, window, N, m0, m0 + bm, bn)
-                    assert 0 <= lo <= hi
-                    for t in range(-(-N // bn)):
-                        full = _expected_class(vis, N, m0, m0 + bm, t * bn, t * bn + bn) == 2
-                        assert full == (lo <= t < hi), (N, bm, bn, m0, t, lo, hi)
+        for vis, offs in _plans(mask, window, N):
+            for bm in (1, 3, 8, 32):
+                for bn in (1, 4, 16, 64):
+                    for m0 in range(0, N, bm):
+                        lo, hi = _lib.attn_full_tile_range(mask, window, N, m0, m0 + bm, bn, offs)
+                        assert 0 <= lo <= hi
+                        for t in range(-(-N // bn)):
+                            full = _expected_class(vis, N, m0, m0 + bm, t * bn, t * bn + bn) == 2
+                            assert full == (lo <= t < hi), (N, offs, bm, bn, m0, t, lo, hi)
+
+
+def test_planner_rejects_bad_host_offsets():
+    for offs in ([1, 8], [0, 7], [0, 5, 3, 8]):
+        assert _lib.attn_tile_class("document", 0, 8, 0, 4, 0, 4, offs) == -1
+        with pytest.raises(ValueError):
+            _lib.attn_k_tile_range("document", 0, 8, 0, 4, 4, offs)
+    with pytest.raises(ValueError):
+        _lib.attn_full_tile_range("document_causal", 0, 8, 0, 4, 4, None)
 
 
 def test_tile_counts_at_workload_sizes():

@@ -43,7 +43,18 @@ def test_paged_inputs_deterministic():
 
 
 def test_workload_table():
-    assert set(wl.WORKLOADS) == {1, 2, 3, 4, 5}
+    assert set(wl.WORKLOADS) == set(range(1, 11))
     w = wl.WORKLOADS[3]
     assert (w.B, w.H, w.N, w.d, w.mask, w.window) == (2, 32, 8192, 128, "sliding", 4096)
     assert abs(wl.WORKLOADS[2].scale - 0.125) == 0
+
+
+def test_document_offsets_recipe():
+    """Offsets start at 0, end at N, every document but the last has a length
+    drawn from [l_min, l_max], and the draw is deterministic per seed."""
+    for N, lo, hi, seed in ((16384, 256, 4096, 1006), (100, 1, 7, 3), (5, 10, 20, 1)):
+        o = wl.document_offsets(N, lo, hi, seed)
+        assert o.dtype == np.int32 and o[0] == 0 and o[-1] == N
+        lens = np.diff(o)
+        assert np.all(lens[:-1] >= lo) and np.all(lens <= hi) and lens[-1] >= 1
+        assert np.array_equal(o, wl.document_offsets(N, lo, hi, seed))

@@ -16,25 +16,26 @@ LIB_PATH = os.path.join(PKG, "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_LAUNCH = range(5)
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = range(3)
-MASKS = {"none": 0, "causal": 1, "sliding": 2}
+MASKS = {"none": 0, "causal": 1, "sliding": 2, "band": 3, "prefix_lm": 4, "document": 5, "document_causal": 6}
+DOC_MASKS = ("document", "document_causal")
 
 # symbol -> (restype, argtypes)
 _c_int, _c_float, _p, _size = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 _PROTOS = {
     "attn_fwd": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
-                          _c_int, _c_int, _p, _p]),
+                          _c_int, _c_int, _p, _c_int, _p, _p]),
     "attn_fwd_fp8": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
-                              _c_int, _c_int, _p, _p]),
+                              _c_int, _c_int, _p, _c_int, _p, _p]),
     "attn_quant_fp8_block": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),
     "attn_decode_paged_workspace_size": (_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_decode_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_float, _p, _p, _size, _p]),
     "attn_gather_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_int, _p]),
-    "attn_tile_class": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
-    "attn_k_tile_range": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+    "attn_tile_class": (_c_int, [_c_int, _c_int, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "attn_k_tile_range": (_c_int, [_c_int, _c_int, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
-    "attn_full_tile_range": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+    "attn_full_tile_range": (_c_int, [_c_int, _c_int, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                       ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "attn_status_str": (ctypes.c_char_p, [_c_int]),
     "attn_abi_version": (_c_int, []),
@@ -103,26 +104,41 @@ def _dev(*ts):
             _require(t.is_cuda and t.is_contiguous(), "tensors must be contiguous GPU tensors")
 
 
-def attn_fwd(q, k, v, o, scale, mask="none", window=0, lse=None, stream=None):
-    """O = softmax(Q K^T * scale, mask) V for q, k, v, o of shape [B, H, N, d]."""
+def _docs(mask, doc_offsets):
+    """(pointer, num_docs) of a device int32 offsets tensor; (None, 0) when unused."""
+    if mask not in DOC_MASKS:
+        return None, 0
+    _require(doc_offsets is not None, f"mask {mask!r} needs doc_offsets")
+    import torch
+    _dev(doc_offsets)
+    _require(doc_offsets.dtype == torch.int32 and doc_offsets.dim() == 1, "doc_offsets must be int32 [num_docs + 1]")
+    return _ptr(doc_offsets), doc_offsets.numel() - 1
+
+
+def attn_fwd(q, k, v, o, scale, mask="none", window=0, doc_offsets=None, lse=None, stream=None):
+    """O = softmax(Q K^T * scale, mask) V for q, k, v, o of shape [B, H, N, d].
+
+    doc_offsets: device int32 [num_docs + 1] for the document masks."""
     _dev(q, k, v, o, lse)
     _require(q.dim() == 4 and q.shape == k.shape == v.shape == o.shape, "q, k, v, o must be [B, H, N, d]")
     _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
     B, H, N, d = q.shape
+    dp, nd = _docs(mask, doc_offsets)
     _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, _dtype_code(q), _dtype_code(o),
-                           float(scale), MASKS[mask], int(window), _ptr(lse), _stream(stream)))
+                           float(scale), MASKS[mask], int(window), dp, nd, _ptr(lse), _stream(stream)))
     return o
 
 
-def attn_fwd_fp8(q8, q_scale, k8, k_scale, v, o, scale, mask="none", window=0, qk_block=128, lse=None,
-                 stream=None):
+def attn_fwd_fp8(q8, q_scale, k8, k_scale, v, o, scale, mask="none", window=0, doc_offsets=None, qk_block=128,
+                 lse=None, stream=None):
     """fp8 block-scaled Q, K (uint8 E4M3FN codes + fp32 block scales), bf16 V and O."""
     _dev(q8, q_scale, k8, k_scale, v, o, lse)
     _require(q8.dim() == 4 and q8.shape == k8.shape == v.shape == o.shape, "shapes must be [B, H, N, d]")
     B, H, N, d = q8.shape
+    dp, nd = _docs(mask, doc_offsets)
     _check(load().attn_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), _ptr(o),
-                               B, H, N, d, int(qk_block), float(scale), MASKS[mask], int(window), _ptr(lse),
-                               _stream(stream)))
+                               B, H, N, d, int(qk_block), float(scale), MASKS[mask], int(window), dp, nd,
+                               _ptr(lse), _stream(stream)))
     return o
 
 
@@ -164,19 +180,33 @@ def attn_gather_paged(k_pool, v_pool, block_table, seq_lens, k_out, v_out, strea
     return k_out, v_out
 
 
-def attn_tile_class(mask, window, N, m0, m1, n0, n1):
-    return int(load().attn_tile_class(MASKS[mask], window, N, m0, m1, n0, n1))
+def _host_docs(doc_offsets):
+    """(ctypes int32 array, num_docs) of host offsets (any int sequence), or (None, 0)."""
+    if doc_offsets is None:
+        return None, 0
+    vals = [int(x) for x in doc_offsets]
+    return (ctypes.c_int32 * len(vals))(*vals), len(vals) - 1
 
 
-def attn_k_tile_range(mask, window, N, m0, m1, bn):
+def attn_tile_class(mask, window, N, m0, m1, n0, n1, doc_offsets=None):
+    """Tile class (0 EMPTY, 1 PARTIAL, 2 FULL; -1 invalid). doc_offsets: host offsets for document masks."""
+    arr, nd = _host_docs(doc_offsets)
+    return int(load().attn_tile_class(MASKS[mask], window, arr, nd, N, m0, m1, n0, n1))
+
+
+def attn_k_tile_range(mask, window, N, m0, m1, bn, doc_offsets=None):
+    arr, nd = _host_docs(doc_offsets)
     lo, hi = _c_int(), _c_int()
-    _check(load().attn_k_tile_range(MASKS[mask], window, N, m0, m1, bn, ctypes.byref(lo), ctypes.byref(hi)))
+    _check(load().attn_k_tile_range(MASKS[mask], window, arr, nd, N, m0, m1, bn, ctypes.byref(lo),
+                                    ctypes.byref(hi)))
     return lo.value, hi.value
 
 
-def attn_full_tile_range(mask, window, N, m0, m1, bn):
+def attn_full_tile_range(mask, window, N, m0, m1, bn, doc_offsets=None):
+    arr, nd = _host_docs(doc_offsets)
     lo, hi = _c_int(), _c_int()
-    _check(load().attn_full_tile_range(MASKS[mask], window, N, m0, m1, bn, ctypes.byref(lo), ctypes.byref(hi)))
+    _check(load().attn_full_tile_range(MASKS[mask], window, arr, nd, N, m0, m1, bn, ctypes.byref(lo),
+                                       ctypes.byref(hi)))
     return lo.value, hi.value
 
 

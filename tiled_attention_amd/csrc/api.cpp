@@ -12,10 +12,37 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool valid_mask(int mask, int window) {
-  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_SLIDING) return false;
-  if (mask == ATTN_MASK_SLIDING && window < 1) return false;
+// Mask kind and window; the document masks also need their offsets array
+// (device or host pointer, 4-byte aligned) and num_docs >= 1.
+bool valid_mask(int mask, int window, const int32_t* doc_offsets, int num_docs) {
+  switch (mask) {
+    case ATTN_MASK_NONE:
+    case ATTN_MASK_CAUSAL: return true;
+    case ATTN_MASK_SLIDING: return window >= 1;
+    case ATTN_MASK_BAND:
+    case ATTN_MASK_PREFIX_LM: return window >= 0;
+    case ATTN_MASK_DOCUMENT:
+    case ATTN_MASK_DOCUMENT_CAUSAL:
+      return doc_offsets != nullptr && ((uintptr_t)doc_offsets & 3u) == 0 && num_docs >= 1 &&
+             num_docs < (1 << 30);
+  }
+  return false;
+}
+
+// Host document offsets: 0 first, N last, never decreasing.
+bool valid_host_docs(const int32_t* offs, int num_docs, int N) {
+  if (offs[0] != 0 || offs[num_docs] != N) return false;
+  for (int d = 0; d < num_docs; ++d)
+    if (offs[d + 1] < offs[d]) return false;
   return true;
+}
+
+// Fills the mask fields of a launch.
+void set_mask(attn::FwdArgs& a, int mask, int window, const int32_t* doc_offsets, int num_docs, int N) {
+  a.mask = mask;
+  a.window = attn::clamp_window(mask, window, N);
+  a.doc = attn::is_document(mask) ? doc_offsets : nullptr;
+  a.num_docs = attn::is_document(mask) ? num_docs : 0;
 }
 
 // Shared size checks: B, H, N >= 1; d > 0; B*H*N fits in 31 bits.
@@ -34,13 +61,13 @@ extern "C" {
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
                      attn_dtype in_dtype, attn_dtype out_dtype, float scale, attn_mask mask, int window,
-                     float* lse, void* stream) {
+                     const int32_t* doc_offsets, int num_docs, float* lse, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
   if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
   if (in_dtype != ATTN_F32 && in_dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
   if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
-  if (!valid_mask(mask, window)) return ATTN_ERR_INVALID_ARG;
+  if (!valid_mask(mask, window, doc_offsets, num_docs)) return ATTN_ERR_INVALID_ARG;
   if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_dims(B, H, N, d);
   if (st != ATTN_OK) return st;
@@ -53,8 +80,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, int B
   a.BH = B * H;
   a.N = N;
   a.d = d;
-  a.mask = mask;
-  a.window = mask == ATTN_MASK_SLIDING ? window : 0;
+  set_mask(a, mask, window, doc_offsets, num_docs, N);
   a.scale = scale;
   a.in_f32 = in_dtype == ATTN_F32;
   a.out_f32 = out_dtype == ATTN_F32;
@@ -64,12 +90,13 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, int B
 
 attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
                          const void* v, void* o, int B, int H, int N, int d, int qk_block, float scale,
-                         attn_mask mask, int window, float* lse, void* stream) {
+                         attn_mask mask, int window, const int32_t* doc_offsets, int num_docs, float* lse,
+                         void* stream) {
   if (!q8 || !q_scale || !k8 || !k_scale || !v || !o) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
   if (((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u)) return ATTN_ERR_INVALID_ARG;
   if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
-  if (!valid_mask(mask, window)) return ATTN_ERR_INVALID_ARG;
+  if (!valid_mask(mask, window, doc_offsets, num_docs)) return ATTN_ERR_INVALID_ARG;
   if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
   if (qk_block < 1) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_dims(B, H, N, d);
@@ -86,8 +113,7 @@ attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t*
   a.BH = B * H;
   a.N = N;
   a.d = d;
-  a.mask = mask;
-  a.window = mask == ATTN_MASK_SLIDING ? window : 0;
+  set_mask(a, mask, window, doc_offsets, num_docs, N);
   a.scale = scale;
   a.in_f32 = false;
   a.out_f32 = false;
@@ -180,23 +206,49 @@ attn_status attn_gather_paged(const void* k_pool, const void* v_pool, const int3
   return launched(attn::launch_gather(a, (hipStream_t)stream));
 }
 
-int attn_tile_class(attn_mask mask, int window, int N, int m0, int m1, int n0, int n1) {
-  if (!valid_mask(mask, window) || N < 1 || m0 < 0 || n0 < 0 || m1 < m0 || n1 < n0) return -1;
-  return attn::tile_class(mask, mask == ATTN_MASK_SLIDING ? window : 0, N, m0, m1, n0, n1);
+// Spans of the first and last rows of [m0, m1) clipped to N (m0 < min(m1, N)).
+static void plan_spans(int mask, int window, const int32_t* offs, int num_docs, int N, int m0, int m1,
+                       attn::KeySpan* first, attn::KeySpan* last) {
+  if (m1 > N) m1 = N;
+  *first = attn::host_span(mask, window, offs, num_docs, N, m0);
+  *last = attn::host_span(mask, window, offs, num_docs, N, m1 - 1);
 }
 
-attn_status attn_k_tile_range(attn_mask mask, int window, int N, int m0, int m1, int bn, int* t_lo, int* t_hi) {
-  if (!t_lo || !t_hi || !valid_mask(mask, window) || N < 1 || bn < 1 || m0 < 0 || m1 < m0)
+static bool valid_plan(int mask, int window, const int32_t* offs, int num_docs, int N) {
+  if (N < 1 || !valid_mask(mask, window, offs, num_docs)) return false;
+  return !attn::is_document(mask) || valid_host_docs(offs, num_docs, N);
+}
+
+int attn_tile_class(attn_mask mask, int window, const int32_t* doc_offsets, int num_docs, int N, int m0, int m1,
+                    int n0, int n1) {
+  if (!valid_plan(mask, window, doc_offsets, num_docs, N) || m0 < 0 || n0 < 0 || m1 < m0 || n1 < n0) return -1;
+  if (m0 >= (m1 < N ? m1 : N)) return attn::TILE_EMPTY;
+  attn::KeySpan first, last;
+  plan_spans(mask, window, doc_offsets, num_docs, N, m0, m1, &first, &last);
+  return attn::span_tile_class(first, last, N, n0, n1);
+}
+
+attn_status attn_k_tile_range(attn_mask mask, int window, const int32_t* doc_offsets, int num_docs, int N, int m0,
+                              int m1, int bn, int* t_lo, int* t_hi) {
+  if (!t_lo || !t_hi || !valid_plan(mask, window, doc_offsets, num_docs, N) || bn < 1 || m0 < 0 || m1 < m0)
     return ATTN_ERR_INVALID_ARG;
-  attn::k_tile_range(mask, mask == ATTN_MASK_SLIDING ? window : 0, N, m0, m1, bn, t_lo, t_hi);
+  *t_lo = *t_hi = 0;
+  if (m0 >= (m1 < N ? m1 : N)) return ATTN_OK;
+  attn::KeySpan first, last;
+  plan_spans(mask, window, doc_offsets, num_docs, N, m0, m1, &first, &last);
+  attn::touched_tiles(first, last, bn, t_lo, t_hi);
   return ATTN_OK;
 }
 
-attn_status attn_full_tile_range(attn_mask mask, int window, int N, int m0, int m1, int bn, int* f_lo,
-                                 int* f_hi) {
-  if (!f_lo || !f_hi || !valid_mask(mask, window) || N < 1 || bn < 1 || m0 < 0 || m1 < m0)
+attn_status attn_full_tile_range(attn_mask mask, int window, const int32_t* doc_offsets, int num_docs, int N,
+                                 int m0, int m1, int bn, int* f_lo, int* f_hi) {
+  if (!f_lo || !f_hi || !valid_plan(mask, window, doc_offsets, num_docs, N) || bn < 1 || m0 < 0 || m1 < m0)
     return ATTN_ERR_INVALID_ARG;
-  attn::full_tile_range(mask, mask == ATTN_MASK_SLIDING ? window : 0, N, m0, m1, bn, f_lo, f_hi);
+  *f_lo = *f_hi = 0;
+  if (m0 >= (m1 < N ? m1 : N)) return ATTN_OK;
+  attn::KeySpan first, last;
+  plan_spans(mask, window, doc_offsets, num_docs, N, m0, m1, &first, &last);
+  attn::full_tiles(first, last, bn, f_lo, f_hi);
   return ATTN_OK;
 }
 

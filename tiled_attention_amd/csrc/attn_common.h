@@ -15,94 +15,183 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
-enum MaskKind { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_SLIDING = 2 };
+enum MaskKind {
+  MASK_NONE = 0,
+  MASK_CAUSAL = 1,
+  MASK_SLIDING = 2,
+  MASK_BAND = 3,
+  MASK_PREFIX_LM = 4,
+  MASK_DOCUMENT = 5,
+  MASK_DOCUMENT_CAUSAL = 6
+};
 enum TileClass { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Window length in keys: SLIDING's window clamped to N + 1 (a longer window
-// sees the same keys), CAUSAL's is N + 1. All mask arithmetic then stays in
-// [-N, 2N] and fits in 32 bits.
-__host__ __device__ inline int effective_window(int mask, int window, int N) {
-  return (mask == MASK_SLIDING && window <= N) ? window : N + 1;
+__host__ __device__ inline bool is_document(int mask) {
+  return mask == MASK_DOCUMENT || mask == MASK_DOCUMENT_CAUSAL;
 }
 
-// Key j visible to query i (both < N)? NONE: always; CAUSAL: j <= i;
-// SLIDING: i - window < j <= i. w is effective_window().
-__host__ __device__ inline bool key_visible(int mask, int w, int i, int j) {
-  if (mask == MASK_NONE) return true;
-  return j <= i && j > i - w;
+// The keys visible to a query row i form one interval [lo, hi] for every mask
+// here: the band masks by definition, the document masks because a document
+// is a run of consecutive positions. The interval holds i itself, and lo and
+// hi never decrease as i grows. Hence the keys visible to some row of
+// [m0, m1) are exactly [lo(m0), hi(m1 - 1)], and the keys visible to every
+// row of it are [lo(m1 - 1), hi(m0)]: tile classification and loop bounds
+// need the spans of the first and last rows only ("Optimizing Triton kernels
+// for custom attention patterns on H100", Patterns A and B).
+struct KeySpan {
+  int lo, hi;
+};
+
+// Window argument clamped to what changes the mask, so that i + window and
+// i - window stay within [-N, 2N] (SLIDING: more than N keys is causal; BAND
+// and PREFIX_LM: N covers every key).
+__host__ __device__ inline int clamp_window(int mask, int window, int N) {
+  if (mask == MASK_SLIDING) return window <= N ? window : N + 1;
+  if (mask == MASK_BAND || mask == MASK_PREFIX_LM) return window <= N ? window : N;
+  return 0;
 }
 
-// Class of the tile (query rows [m0, m1)) x (keys [n0, n1)).
-// Rows >= N are ignored; keys >= N do not exist (a tile reaching past N is
-// at most PARTIAL). The visible region of a causal/sliding mask is a band
-// monotone in i, so the tile misses it iff it lies wholly above the diagonal
-// (n0 > last row) or wholly below the window (last key < first row - w + 1),
-// and lies inside it iff the last key is <= the first row and the first key
-// is > last row - w.
-__host__ __device__ inline int tile_class(int mask, int window, int N, int m0, int m1, int n0,
-                                          int n1) {
-  if (m1 > N) m1 = N;
-  if (m0 >= m1 || n0 >= N || n0 >= n1) return TILE_EMPTY;
+// Span of row i for the closed-form masks (window already clamped).
+//   NONE: every key. CAUSAL: j <= i. SLIDING: i - w < j <= i.
+//   BAND: |i - j| <= w. PREFIX_LM: j <= i or j < w.
+__host__ __device__ inline KeySpan band_span(int mask, int w, int N, int i) {
+  switch (mask) {
+    case MASK_NONE: return {0, N - 1};
+    case MASK_SLIDING: return {i - w + 1 > 0 ? i - w + 1 : 0, i};
+    case MASK_BAND: return {i - w > 0 ? i - w : 0, i + w < N - 1 ? i + w : N - 1};
+    case MASK_PREFIX_LM: return {0, w - 1 > i ? w - 1 : i};
+    default: return {0, i};  // CAUSAL
+  }
+}
+
+// Span of row i inside the document [start, end). Out-of-range offsets are
+// clamped so that the span always holds i and stays inside [0, N): any
+// offsets array then gives in-bounds loop ranges.
+__host__ __device__ inline KeySpan doc_span(bool causal, int start, int end, int N, int i) {
+  KeySpan s;
+  s.lo = start < 0 ? 0 : (start > i ? i : start);
+  if (causal) {
+    s.hi = i;
+  } else {
+    const int e = end > N ? N : end;
+    s.hi = (e > i + 1 ? e : i + 1) - 1;
+  }
+  return s;
+}
+
+// Host: span of row i of any mask; offs / nd describe the documents (host
+// memory): row i lies in the last document d with offs[d] <= i.
+inline KeySpan host_span(int mask, int window, const int32_t* offs, int nd, int N, int i) {
+  if (!is_document(mask)) return band_span(mask, clamp_window(mask, window, N), N, i);
+  int lo = 0, hi = nd - 1;  // the document is the last d in [0, nd) with offs[d] <= i
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (offs[mid] <= i)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return doc_span(mask == MASK_DOCUMENT_CAUSAL, offs[lo], offs[lo + 1], N, i);
+}
+
+// Tiles of bn keys [lo, hi) that hold a key visible to some row whose spans
+// of the first and last rows are `first` and `last`.
+__host__ __device__ inline void touched_tiles(KeySpan first, KeySpan last, int bn, int* lo, int* hi) {
+  *lo = first.lo / bn;
+  *hi = last.hi / bn + 1;
+}
+
+// Tiles [lo, hi) of bn keys in which every pair is visible to every row of
+// the rows with those first/last spans (a contiguous run; empty as lo == hi).
+__host__ __device__ inline void full_tiles(KeySpan first, KeySpan last, int bn, int* lo, int* hi) {
+  const int l = (last.lo + bn - 1) / bn;
+  const int h = (first.hi + 1) / bn;
+  *lo = l < h ? l : h;
+  *hi = h;
+}
+
+// Class of the tile (rows [m0, m1), clipped to N, with those first / last
+// spans) x (keys [n0, n1)). Keys >= N do not exist, so a tile reaching past N
+// is at most PARTIAL.
+__host__ __device__ inline int span_tile_class(KeySpan first, KeySpan last, int N, int n0, int n1) {
+  if (n0 >= N || n0 >= n1) return TILE_EMPTY;
   const bool ragged = n1 > N;
   const int n_last = (ragged ? N : n1) - 1;
-  if (mask == MASK_NONE) return ragged ? TILE_PARTIAL : TILE_FULL;
-  const int w = effective_window(mask, window, N);
-  if (n0 > m1 - 1) return TILE_EMPTY;
-  if (n_last < m0 - w + 1) return TILE_EMPTY;
-  if (!ragged && n_last <= m0 && n0 > (m1 - 1) - w) return TILE_FULL;
+  if (n0 > last.hi || n_last < first.lo) return TILE_EMPTY;
+  if (!ragged && last.lo <= n0 && n_last <= first.hi) return TILE_FULL;
   return TILE_PARTIAL;
 }
 
-// K-tile index range [lo, hi) of tiles of bn keys that may hold a key visible
-// to a row of [m0, m1). Causal: keys <= m1-1. Sliding: keys >= m0 - w + 1.
-__host__ __device__ inline void k_tile_range(int mask, int window, int N, int m0, int m1, int bn,
-                                             int* lo, int* hi) {
-  const int nt = (N + bn - 1) / bn;
-  if (m1 > N) m1 = N;
-  if (m0 >= m1) {
-    *lo = 0;
-    *hi = 0;
-    return;
+// Number of entries <= x among offs[0..n), n >= 1, offs ascending, x the same
+// in every lane of the wave. A 64-ary search: each level probes 64 evenly
+// spaced entries (one load per lane) and a ballot counts those <= x, so the
+// answer is found in ceil(log64(n)) + 1 rounds of independent loads. Reads
+// stay inside offs[0..n) whatever its contents.
+__device__ inline int doc_count_le(const int32_t* offs, int n, int x) {
+  const int lane = __lane_id();
+  int base = 0, span = n;
+  while (span > 64) {
+    const int stride = (span + 63) >> 6;
+    const int pos = base + (lane + 1) * stride - 1;
+    const bool le = pos < base + span && offs[pos] <= x;
+    const int k = __popcll(__ballot(le));
+    base += k * stride;
+    span = min(stride - 1, span - k * stride);
   }
-  if (mask == MASK_NONE) {
-    *lo = 0;
-    *hi = nt;
-    return;
-  }
-  int h = (m1 - 1) / bn + 1;
-  if (h > nt) h = nt;
-  int first = mask == MASK_SLIDING ? m0 - effective_window(mask, window, N) + 1 : 0;
-  if (first < 0) first = 0;
-  *lo = first / bn;
-  *hi = h;
+  const bool le = lane < span && offs[base + lane] <= x;
+  return base + __popcll(__ballot(le));
 }
 
-// Global K-tile index range [lo, hi) of tiles of bn keys that are FULL (every
-// pair visible) for the rows [m0, m1): wholly inside [0, N), every key at or
-// before the first row (causal/sliding), and every key inside the last row's
-// window (sliding). A band mask's FULL tiles are contiguous.
-__host__ __device__ inline void full_tile_range(int mask, int window, int N, int m0, int m1, int bn, int* lo,
-                                                int* hi) {
-  if (m1 > N) m1 = N;
-  if (m0 >= m1) {
-    *lo = 0;
-    *hi = 0;
-    return;
+// Document of row x given count = doc_count_le(offs, nd + 1, x), clamped to a
+// valid document index.
+__device__ inline int doc_index(int count, int nd) {
+  const int d = count - 1;
+  return d < 0 ? 0 : (d > nd - 1 ? nd - 1 : d);
+}
+
+// Spans a workgroup and its waves need, for rows of one wave:
+//   tile_first / tile_last: first and last row of the workgroup's Q tile,
+//   wave_first / wave_last: first and last row of this wave,
+//   lane: this lane's row.
+// Every row argument is < N; all but `row` are uniform across the wave.
+struct RowSpans {
+  KeySpan lane, wave_first, wave_last, tile_first, tile_last;
+};
+
+__device__ inline RowSpans row_spans(int mask, int window, const int32_t* offs, int nd, int N, int tile_r0,
+                                     int tile_r1, int wave_r0, int wave_r1, int row) {
+  RowSpans r;
+  if (!is_document(mask)) {
+    r.lane = band_span(mask, window, N, row);
+    r.wave_first = band_span(mask, window, N, wave_r0);
+    r.wave_last = band_span(mask, window, N, wave_r1);
+    r.tile_first = band_span(mask, window, N, tile_r0);
+    r.tile_last = band_span(mask, window, N, tile_r1);
+    return r;
   }
-  int h = N / bn;
-  int l = 0;
-  if (mask != MASK_NONE) {
-    const int c = (m0 + 1) / bn;  // n1 - 1 <= m0
-    if (c < h) h = c;
-    const int first = m1 - effective_window(mask, window, N);  // n0 >= m1 - w
-    if (first > 0) l = (first + bn - 1) / bn;
-  }
-  if (l > h) l = h;
-  *lo = l;
-  *hi = h;
+  const bool causal = mask == MASK_DOCUMENT_CAUSAL;
+  const int ct0 = doc_count_le(offs, nd + 1, tile_r0);
+  const int ct1 = doc_count_le(offs, nd + 1, tile_r1);
+  const int cw0 = doc_count_le(offs, nd + 1, wave_r0);
+  const int cw1 = doc_count_le(offs, nd + 1, wave_r1);
+  int d = doc_index(ct0, nd);
+  r.tile_first = doc_span(causal, offs[d], offs[d + 1], N, tile_r0);
+  d = doc_index(ct1, nd);
+  r.tile_last = doc_span(causal, offs[d], offs[d + 1], N, tile_r1);
+  d = doc_index(cw0, nd);
+  r.wave_first = doc_span(causal, offs[d], offs[d + 1], N, wave_r0);
+  d = doc_index(cw1, nd);
+  r.wave_last = doc_span(causal, offs[d], offs[d + 1], N, wave_r1);
+  // this lane's row: the document starts between the wave's first and last
+  // rows (usually none or one) decide it
+  int c = cw0;
+  for (int t = cw0; t < cw1; ++t) c += offs[t] <= row ? 1 : 0;
+  d = doc_index(c, nd);
+  r.lane = doc_span(causal, offs[d], offs[d + 1], N, row);
+  return r;
 }
 
 // Workgroup id -> work unit, so that consecutive units land on one XCD.

@@ -29,11 +29,12 @@ struct ParamsF {
   const float* v;
   void* o;
   float* lse;
-  int N, window, n_qtiles;
+  const int32_t* doc;
+  int N, mask, window, nd, n_qtiles;
   float scale_log2;
 };
 
-template <int D, int MASK, bool OUT_F32>
+template <int D, bool OUT_F32>
 __global__ __launch_bounds__(NTF) void fwd_f32_kernel(ParamsF p) {
   constexpr int HALF = D / 2;
   constexpr int PITCH = D + 4;  // floats; keeps 16-byte row starts off one bank
@@ -50,7 +51,10 @@ __global__ __launch_bounds__(NTF) void fwd_f32_kernel(ParamsF p) {
   const int m1 = min(m0 + BMF, N);
   const int qrow = m0 + row_in;
   const size_t head = (size_t)bh * N;
-  const int wlen = effective_window(MASK, p.window, N);
+  // keys visible to this thread's row: [span.lo, span.hi]; a wave holds 32 rows
+  const int wrow0 = m0 + 32 * __builtin_amdgcn_readfirstlane(tid >> 6);
+  const RowSpans sp = row_spans(p.mask, p.window, p.doc, p.nd, N, m0, m1 - 1, min(wrow0, N - 1),
+                                min(wrow0 + 31, N - 1), min(qrow, N - 1));
 
   float q[HALF];
   float acc[HALF];
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(NTF) void fwd_f32_kernel(ParamsF p) {
   float m_run = -INFINITY, l_run = 0.f;
 
   int t_lo, t_hi;
-  k_tile_range(MASK, p.window, N, m0, m1, BNF, &t_lo, &t_hi);
+  touched_tiles(sp.tile_first, sp.tile_last, BNF, &t_lo, &t_hi);
   constexpr int CH = D / 4;  // float4 per row
   for (int kt = t_lo; kt < t_hi; ++kt) {
     const int n0 = kt * BNF;
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(NTF) void fwd_f32_kernel(ParamsF p) {
       }
       dot += __shfl_xor(dot, 1);
       const int key = n0 + j;
-      s[j] = (key < N && key_visible(MASK, wlen, qrow, key)) ? dot : -INFINITY;
+      s[j] = (key >= sp.lane.lo && key <= sp.lane.hi) ? dot : -INFINITY;
     }
     float mx = s[0];
 #pragma unroll
@@ -146,21 +150,15 @@ hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
   p.v = (const float*)a.v;
   p.o = a.o;
   p.lse = a.lse;
+  p.doc = a.doc;
   p.N = a.N;
+  p.mask = a.mask;
   p.window = a.window;
+  p.nd = a.num_docs;
   p.n_qtiles = (a.N + BMF - 1) / BMF;
   p.scale_log2 = a.scale * kLog2e;
   dim3 grid(p.n_qtiles, a.BH);
-  switch (a.mask) {
-    case MASK_NONE:
-      hipLaunchKernelGGL((fwd_f32_kernel<D, MASK_NONE, OUT_F32>), grid, dim3(NTF), 0, stream, p);
-      break;
-    case MASK_CAUSAL:
-      hipLaunchKernelGGL((fwd_f32_kernel<D, MASK_CAUSAL, OUT_F32>), grid, dim3(NTF), 0, stream, p);
-      break;
-    default:
-      hipLaunchKernelGGL((fwd_f32_kernel<D, MASK_SLIDING, OUT_F32>), grid, dim3(NTF), 0, stream, p);
-  }
+  hipLaunchKernelGGL((fwd_f32_kernel<D, OUT_F32>), grid, dim3(NTF), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -41,13 +41,18 @@
 //    l and acc by 2^(m_old - m_new). O = acc / l does not depend on the
 //    reference used. l sums P in fp32 with plain adds; P V applies P rounded
 //    to bf16, so the weights O uses sum to 1 within the bf16 rounding of P.
-//  * Per wave, the K tiles fully inside the mask form one contiguous range
-//    (two scalar bounds); only tiles outside it evaluate the mask, and the
-//    tile loop never visits tiles outside the mask's band ("Optimizing Triton
-//    kernels for custom attention patterns on H100", Pattern B: loop bounds
-//    and edge-only masking).
-//  * Causal: a workgroup takes Q tiles t and T-1-t so all carry equal work;
-//    workgroup ids are mapped so that a head's tiles share an XCD (its L2).
+//  * Masks: the keys a row sees form one interval whose ends never decrease
+//    with the row (every mask kind, documents included), so the tiles the
+//    workgroup must visit and the tiles fully visible to a wave's 32 rows are
+//    two contiguous ranges set once per Q tile; only tiles outside the
+//    latter evaluate the mask, as a compare of each key against the lane's
+//    interval ("Optimizing Triton kernels for custom attention patterns on
+//    H100", Patterns A and B: loop bounds, edge-only masking, document bounds
+//    found by a search of the document offsets). The mask kind is a run-time
+//    value: it only changes this set-up.
+//  * Causal and prefix-LM: a workgroup takes Q tiles t and T-1-t so all carry
+//    about equal work; workgroup ids are mapped so that a head's tiles share
+//    an XCD (its L2).
 #include <type_traits>
 #include <utility>
 
@@ -109,7 +114,8 @@ struct Params {
   float* lse;
   const float* q_scale;
   const float* k_scale;
-  int N, window, n_qtiles, units_per_bh, units, pair, nsb;
+  const int32_t* doc;
+  int N, mask, window, nd, n_qtiles, units_per_bh, units, pair, nsb;
   float scale_log2;
 };
 
@@ -169,7 +175,7 @@ struct TileStream {
   }
 };
 
-template <int D, int MASK, bool FP8, bool OUT_F32>
+template <int D, bool FP8, bool OUT_F32>
 struct QTile {
   using C = Cfg<D, FP8>;
   static constexpr int KROW = C::KROW, VROW = C::VROW, QK_STEPS = C::QK_STEPS, DE = C::DE;
@@ -182,7 +188,8 @@ struct QTile {
 
   const Params& p;
   unsigned char* smem;
-  int lane, wave, l32, hl, N, bh, m0, wrow0, qrow, qsrc, t_lo, NK, wlen;
+  int lane, wave, l32, hl, N, bh, m0, wrow0, qrow, qsrc, t_lo, NK;
+  int klo_m1, khi;          // keys visible to the lane's row: klo_m1 < key <= khi
   int f_lo, f_hi;           // local tiles [f_lo, f_hi) are FULL for this wave
   size_t head;
   QFrag qf[QK_STEPS];
@@ -219,11 +226,18 @@ struct QTile {
     qsrc = min(qrow, N - 1);
     head = (size_t)bh * N;
 
-    k_tile_range(MASK, p.window, N, m0, m1, BN, &t_lo, &NK);
+    const int wr0 = min(wrow0, N - 1), wr1 = min(wrow0 + 31, N - 1);
+    const RowSpans sp = row_spans(p.mask, p.window, p.doc, p.nd, N, m0, m1 - 1, wr0, wr1, qsrc);
+    touched_tiles(sp.tile_first, sp.tile_last, BN, &t_lo, &NK);
     NK -= t_lo;
-    wlen = effective_window(MASK, p.window, N);
-    // FULL range of this wave's 32 rows (a contiguous run of the band's tiles), local indices
-    full_tile_range(MASK, p.window, N, wrow0, wrow0 + 32, BN, &f_lo, &f_hi);
+    // opaque to the optimizer: bounds it can reason about (NK >= 1, t_lo = 0
+    // for causal masks) let it restructure the tile loop of the fp8 kernels
+    // in a way that overflows the VGPRs
+    asm volatile("" : "+s"(t_lo), "+s"(NK));
+    klo_m1 = sp.lane.lo - 1;
+    khi = sp.lane.hi;
+    // FULL range of this wave's 32 rows (a contiguous run of tiles), local indices
+    full_tiles(sp.wave_first, sp.wave_last, BN, &f_lo, &f_hi);
     f_lo = min(max(f_lo - t_lo, 0), NK);
     f_hi = min(max(f_hi - t_lo, f_lo), NK);
     qscale = 1.f;
@@ -380,10 +394,10 @@ struct QTile {
   template <int B>
   __device__ __forceinline__ void mask(int i) {
     // key of S[B][b][r] is n0 + 32b + 8(r/4) + 4hl + r%4
-    // visible offsets kc: lo < kc <= hi (keys past N do not exist)
+    // visible offsets kc: lo < kc <= hi (the interval ends before N)
     const int n0 = (t_lo + i) * BN + 4 * hl;
-    const int hi = (MASK == MASK_NONE ? N - 1 : qsrc) - n0;
-    const int lo = MASK == MASK_NONE ? -1 : qsrc - wlen - n0;
+    const int hi = khi - n0;
+    const int lo = klo_m1 - n0;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -572,7 +586,7 @@ struct QTile {
   }
 };
 
-template <int D, int MASK, bool FP8, bool OUT_F32>
+template <int D, bool FP8, bool OUT_F32>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8>::LDS];
   const int u = xcd_unit(blockIdx.x, gridDim.x);
@@ -583,14 +597,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // the Q loads, so the two latencies overlap)
   const int ta = w, tb = p.n_qtiles - 1 - w;
   {
-    QTile<D, MASK, FP8, OUT_F32> a(p, smem, bh, tb);
+    QTile<D, FP8, OUT_F32> a(p, smem, bh, tb);
     a.start_stream();
     a.load_q();
     a.loop();
     a.epilogue();
   }
   if (p.pair && ta != tb) {
-    QTile<D, MASK, FP8, OUT_F32> b(p, smem, bh, ta);
+    QTile<D, FP8, OUT_F32> b(p, smem, bh, ta);
     b.start_stream();
     b.load_q();
     b.loop();
@@ -598,7 +612,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
-template <int D, int MASK, bool FP8, bool OUT_F32>
+template <int D, bool FP8, bool OUT_F32>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   Params p;
   p.q = a.q;
@@ -608,38 +622,32 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.lse = a.lse;
   p.q_scale = a.q_scale;
   p.k_scale = a.k_scale;
+  p.doc = a.doc;
   p.N = a.N;
+  p.mask = a.mask;
   p.window = a.window;
+  p.nd = a.num_docs;
   p.n_qtiles = (a.N + BM - 1) / BM;
-  p.pair = (MASK == MASK_CAUSAL) ? 1 : 0;
+  p.pair = (a.mask == MASK_CAUSAL || a.mask == MASK_PREFIX_LM) ? 1 : 0;
   p.units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   p.units = a.BH * p.units_per_bh;
   p.nsb = (a.N + 127) / 128;
   p.scale_log2 = a.scale * kLog2e;
   const int grid = round_up8(p.units);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, MASK, FP8, OUT_F32>), dim3(grid), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32>), dim3(grid), dim3(NT), 0, stream, p);
   return hipGetLastError();
-}
-
-template <int D, bool FP8, bool OUT_F32>
-hipError_t launch_mask(const FwdArgs& a, hipStream_t stream) {
-  switch (a.mask) {
-    case MASK_NONE: return launch_t<D, MASK_NONE, FP8, OUT_F32>(a, stream);
-    case MASK_CAUSAL: return launch_t<D, MASK_CAUSAL, FP8, OUT_F32>(a, stream);
-    default: return launch_t<D, MASK_SLIDING, FP8, OUT_F32>(a, stream);
-  }
 }
 
 }  // namespace
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t stream) {
   if (a.fp8) {
-    return a.d == 64 ? launch_mask<64, true, false>(a, stream) : launch_mask<128, true, false>(a, stream);
+    return a.d == 64 ? launch_t<64, true, false>(a, stream) : launch_t<128, true, false>(a, stream);
   }
   if (a.out_f32) {
-    return a.d == 64 ? launch_mask<64, false, true>(a, stream) : launch_mask<128, false, true>(a, stream);
+    return a.d == 64 ? launch_t<64, false, true>(a, stream) : launch_t<128, false, true>(a, stream);
   }
-  return a.d == 64 ? launch_mask<64, false, false>(a, stream) : launch_mask<128, false, false>(a, stream);
+  return a.d == 64 ? launch_t<64, false, false>(a, stream) : launch_t<128, false, false>(a, stream);
 }
 
 }  // namespace attn

@@ -15,7 +15,9 @@ struct FwdArgs {
   float* lse;           // nullable
   const float* q_scale; // fp8 only: [BH, ceil(N/128)]
   const float* k_scale;
-  int BH, N, d, mask, window;
+  const int32_t* doc;   // document masks: [num_docs + 1] start offsets
+  int num_docs;
+  int BH, N, d, mask, window;  // window clamped (clamp_window)
   float scale;
   bool in_f32, out_f32, fp8;
 };

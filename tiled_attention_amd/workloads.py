@@ -21,6 +21,10 @@ Recipe (all draws from ``numpy.random.default_rng(seed)``):
   of the P = sum ceil(L_s/16) + spare page ids, handed out in (sequence, slot)
   order. Unused rows of last pages and spare pages hold NaN; block-table
   entries past a sequence's last page hold -1.
+* documents: document lengths ``integers(l_min, l_max, endpoint=True)`` from
+  ``numpy.random.default_rng([seed, 1])`` (a stream apart from Q, K, V), drawn
+  until they cover N; the last document is cut at N. The offsets are the
+  running sums, starting at 0 and ending at N.
 * bf16 values are the fp32 draws rounded to nearest-even once, on the host
   (``torch.Tensor.to(torch.bfloat16)``), before either side sees them.
 """
@@ -71,6 +75,20 @@ WORKLOADS = {
                 n_seq=64, l_min=512, l_max=8192),
     5: Workload(5, "fp8_causal_b1_h16_n16384_d128", "fp8", B=1, H=16, N=16384, d=128,
                 mask="causal", outlier_p=0.01, outlier_scale=20.0),
+    # structured masks ("Optimizing Triton kernels ...", Patterns A and B):
+    # documents of 256..4096 tokens packed into 16K positions, the same as a
+    # packed batch of causal sequences, a +-4096 window over 32K positions,
+    # a 2048-token prefix, and the unmasked 16K shape the document kernel is
+    # compared with
+    6: Workload(6, "document_bf16_b1_h16_n16384_d128_docs256to4096", "dense", B=1, H=16, N=16384, d=128,
+                mask="document", l_min=256, l_max=4096),
+    7: Workload(7, "varlen_causal_bf16_b1_h16_n16384_d128_seqs256to4096", "dense", B=1, H=16, N=16384,
+                d=128, mask="document_causal", l_min=256, l_max=4096),
+    8: Workload(8, "band4096_bf16_b1_h16_n32768_d128", "dense", B=1, H=16, N=32768, d=128,
+                mask="band", window=4096),
+    9: Workload(9, "prefix_lm2048_bf16_b2_h16_n8192_d128", "dense", B=2, H=16, N=8192, d=128,
+                mask="prefix_lm", window=2048),
+    10: Workload(10, "dense_bf16_b1_h16_n16384_d128", "dense", B=1, H=16, N=16384, d=128, mask="none"),
 }
 
 
@@ -100,6 +118,15 @@ def dense_inputs(B, H, N, d, seed, outlier_p=0.0, outlier_scale=1.0):
             sel = rng.random(shape) < outlier_p
             x[sel] *= np.float32(outlier_scale)
     return q, k, v
+
+
+def document_offsets(N, l_min, l_max, seed):
+    """Document start offsets int32 [num_docs + 1] covering N positions."""
+    rng = np.random.default_rng([seed, 1])
+    offs = [0]
+    while offs[-1] < N:
+        offs.append(min(N, offs[-1] + int(rng.integers(l_min, l_max, endpoint=True))))
+    return np.array(offs, dtype=np.int32)
 
 
 @dataclass
