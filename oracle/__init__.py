@@ -20,8 +20,10 @@ Modules and the passages they follow (pages cited by title and section):
   m, running sum l, rescale by exp(m - m_new)) and the merge of partial
   results. "Flash MSA ...", "Understanding Flash MSA Core Mechanics" and the
   kernel listing in "Implementation Step-by-Step with Triton".
-* ``paged``      -- block-table page gather and single-query decode over it.
-  "Optimizing Triton kernels ...", Pattern C (gather_pages).
+* ``paged``      -- block-table page gather, single-query decode, causal
+  prefill of the last rows of a paged sequence, and block-sparse paged
+  cross-attention (each query block over its own page list).
+  "Optimizing Triton kernels ...", Pattern C (gather_pages and its uses).
 * ``fp8``        -- OCP E4M3FN encode/decode and per-128-row-block
   quantisation with scale = block absmax / 448. "FlashAttention-3: Warp
   Specialization ...", section "FP8 Block Quantization".
@@ -33,14 +35,14 @@ invariants, brute force or independent library routines; none is marked
 
 from .attention import visible, attention, probabilities, visible_pair_count
 from .recurrence import tiled_attention, partial_state, merge_partials, split_attention
-from .paged import gather, decode
+from .paged import gather, decode, prefill, cross, listed_keys
 from .fp8 import (E4M3_MAX, e4m3_value, e4m3_table, e4m3_encode, quantize_blocks,
                   dequantize_blocks)
 
 __all__ = [
     "visible", "attention", "probabilities", "visible_pair_count",
     "tiled_attention", "partial_state", "merge_partials", "split_attention",
-    "gather", "decode",
+    "gather", "decode", "prefill", "cross", "listed_keys",
     "E4M3_MAX", "e4m3_value", "e4m3_table", "e4m3_encode", "quantize_blocks",
     "dequantize_blocks",
 ]

@@ -243,6 +243,65 @@ def test_paged_gather_round_trip_and_decode():
         assert np.max(np.abs(lse[s] - lse_c[:, -1])) <= 1e-12
 
 
+def test_paged_prefill_is_the_last_rows_of_causal_attention():
+    """Prefill of the last q_len positions equals the last q_len rows of plain
+    causal attention on the dense sequence, and q_len = 1 equals decode."""
+    from tiled_attention_amd.workloads import paged_inputs, bf16_to_f64
+    for page in (16, 64):
+        inp = paged_inputs(n_seq=4, H=2, d=8, l_min=5, l_max=150, seed=21, spare=3, keep_dense=True,
+                           page_size=page, q_rows=5)
+        kp, vp = inp.k_pool.float().numpy(), inp.v_pool.float().numpy()
+        q = bf16_to_f64(inp.q)
+        o, lse = oracle.prefill(q, kp, vp, inp.block_table.numpy(), inp.seq_lens.numpy(), 0.4, page_size=page)
+        assert np.isfinite(o).all()
+        for s in range(4):
+            L = int(inp.seq_lens[s])
+            qfull = np.concatenate([np.zeros((2, L - 5, 8)), q[s]], axis=1)
+            o_c, lse_c = oracle.attention(qfull, bf16_to_f64(inp.k_dense[s]), bf16_to_f64(inp.v_dense[s]), 0.4,
+                                          "causal")
+            assert np.max(np.abs(o[s] - o_c[:, -5:])) <= 1e-12
+            assert np.max(np.abs(lse[s] - lse_c[:, -5:])) <= 1e-12
+        o1, lse1 = oracle.prefill(q[:, :, -1:], kp, vp, inp.block_table.numpy(), inp.seq_lens.numpy(), 0.4,
+                                  page_size=page)
+        od, lsed = oracle.decode(q[:, :, -1], kp, vp, inp.block_table.numpy(), inp.seq_lens.numpy(), 0.4,
+                                 page_size=page)
+        assert np.max(np.abs(o1[:, :, 0] - od)) <= 1e-12 and np.max(np.abs(lse1[:, :, 0] - lsed)) <= 1e-12
+
+
+def test_paged_cross_attention_pins():
+    """Listed keys are the concatenated pages; a query block listing a
+    sequence's pages in order sees its dense keys; permuting whole pages
+    changes nothing (keys are unordered without a mask); no keys give 0 / -inf."""
+    from tiled_attention_amd.workloads import paged_cross_inputs, bf16_to_f64
+    inp = paged_cross_inputs(n_seq=2, H=2, d=8, q_len=300, pool_pages=9, pages_per_block=4, seed=5,
+                             page_size=16, q_block=128)
+    kp, vp = inp.k_pool.float().numpy(), inp.v_pool.float().numpy()
+    table, lens = inp.page_table.numpy(), inp.kv_lens.numpy()
+    assert table.shape == (2, 3, 4) and np.all(lens > 48) and np.all(lens <= 64)
+    pages = table[1, 2]
+    want = np.concatenate([kp[p] for p in pages], axis=1)[:, :int(lens[1, 2])]
+    assert np.array_equal(oracle.listed_keys(kp, pages, int(lens[1, 2]), 16), want)
+    q = bf16_to_f64(inp.q)
+    o, lse = oracle.cross(q, kp, vp, table, lens, 0.3, page_size=16, q_block=128)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for s in range(2):
+        for b in range(3):
+            r = slice(128 * b, min(300, 128 * b + 128))
+            k = np.concatenate([kp[p] for p in table[s, b]], axis=1)[:, :lens[s, b]]
+            v = np.concatenate([vp[p] for p in table[s, b]], axis=1)[:, :lens[s, b]]
+            o_d, _ = oracle.attention(q[s, :, r], k, v, 0.3, "none")
+            assert np.max(np.abs(o[s, :, r] - o_d)) <= 1e-12
+    full = np.full_like(lens, 64)
+    o_f, _ = oracle.cross(q, kp, vp, table, full, 0.3, page_size=16, q_block=128)
+    o_p, _ = oracle.cross(q, kp, vp, table[:, :, ::-1], full, 0.3, page_size=16, q_block=128)
+    assert np.max(np.abs(o_f - o_p)) <= 1e-12
+    none = lens.copy()
+    none[0, 1] = 0
+    o_n, lse_n = oracle.cross(q, kp, vp, table, none, 0.3, page_size=16, q_block=128)
+    assert np.all(o_n[0, :, 128:256] == 0) and np.all(lse_n[0, :, 128:256] == -np.inf)
+    assert np.array_equal(o_n[1], o[1])
+
+
 def test_paged_layout_shapes_and_poison():
     from tiled_attention_amd.workloads import paged_inputs
     inp = paged_inputs(n_seq=4, H=2, d=4, l_min=1, l_max=40, seed=11, spare=3)

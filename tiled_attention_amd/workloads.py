@@ -142,11 +142,13 @@ class PagedInputs:
 
 
 def paged_inputs(n_seq, H, d, l_min, l_max, seed, page_size=16, spare=64, max_pages=None,
-                 keep_dense=False):
-    """A shuffled paged KV pool with per-sequence block tables."""
+                 keep_dense=False, q_rows=None):
+    """A shuffled paged KV pool with per-sequence block tables. Q is [S, H, d]
+    (one decode query per sequence), or [S, H, q_rows, d] for a prefill of the
+    last q_rows positions."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(l_min, l_max, size=n_seq, endpoint=True).astype(np.int64)
-    q = rng.standard_normal((n_seq, H, d), dtype=np.float32)
+    q = rng.standard_normal((n_seq, H, d) if q_rows is None else (n_seq, H, q_rows, d), dtype=np.float32)
     pages_per_seq = (lens + page_size - 1) // page_size
     if max_pages is None:
         max_pages = -(-l_max // page_size)
@@ -178,6 +180,45 @@ def paged_inputs(n_seq, H, d, l_min, l_max, seed, page_size=16, spare=64, max_pa
     if keep_dense:
         out.k_dense, out.v_dense = k_dense, v_dense
     return out
+
+
+@dataclass
+class CrossInputs:
+    q: torch.Tensor               # [S, H, q_len, d] bf16
+    k_pool: torch.Tensor          # [P, H, page, d] bf16
+    v_pool: torch.Tensor
+    page_table: torch.Tensor      # [S, QB, max_pages] int32, -1 padded
+    kv_lens: torch.Tensor         # [S, QB] int32
+    page_size: int
+    q_block: int
+
+
+def paged_cross_inputs(n_seq, H, d, q_len, pool_pages, pages_per_block, seed, page_size=64, q_block=128,
+                       spare=16, ragged=True):
+    """Block-sparse paged cross-attention inputs: a pool of pool_pages pages of
+    random keys/values (plus `spare` NaN-poisoned pages no list names), and for
+    each query block of each sequence a list of pages_per_block distinct pages
+    drawn without replacement; with `ragged`, the block attends to all but the
+    last 0..page_size-1 tokens of its list. Draw order: Q, K pool, V pool, then
+    per (sequence, block) the page choice and the cut."""
+    rng = np.random.default_rng(seed)
+    n_qb = -(-q_len // q_block)
+    q = rng.standard_normal((n_seq, H, q_len, d), dtype=np.float32)
+    kp = rng.standard_normal((pool_pages, H, page_size, d), dtype=np.float32)
+    vp = rng.standard_normal((pool_pages, H, page_size, d), dtype=np.float32)
+    k_pool = torch.full((pool_pages + spare, H, page_size, d), float("nan"), dtype=torch.bfloat16)
+    v_pool = torch.full((pool_pages + spare, H, page_size, d), float("nan"), dtype=torch.bfloat16)
+    k_pool[:pool_pages] = to_bf16(kp)
+    v_pool[:pool_pages] = to_bf16(vp)
+    table = np.full((n_seq, n_qb, pages_per_block), -1, dtype=np.int32)
+    lens = np.zeros((n_seq, n_qb), dtype=np.int32)
+    for s in range(n_seq):
+        for b in range(n_qb):
+            table[s, b] = rng.choice(pool_pages, size=pages_per_block, replace=False)
+            cut = int(rng.integers(0, page_size)) if ragged else 0
+            lens[s, b] = pages_per_block * page_size - cut
+    return CrossInputs(q=to_bf16(q), k_pool=k_pool, v_pool=v_pool, page_table=torch.from_numpy(table),
+                       kv_lens=torch.from_numpy(lens), page_size=page_size, q_block=q_block)
 
 
 def tensor_digest(*tensors):
