@@ -185,6 +185,77 @@ class Paged:
                 "seed": self.seed}
 
 
+class PagedPrefill:
+    """attn_prefill_paged over 64-token pages; also times the page gather a
+    two-stage (gather, then attend) route would add."""
+
+    def __init__(self, key, seed):
+        import torch
+        from tiled_attention_amd import _lib as A
+        from tiled_attention_amd import workloads as wl
+        self.w = w = wl.WORKLOADS[key]
+        self.seed = seed
+        inp = wl.paged_inputs(w.n_seq, w.H, w.d, w.l_min, w.l_max, seed=seed, page_size=w.page_size,
+                              spare=w.spare_pages, q_rows=w.q_len)
+        self.q = inp.q.cuda()
+        self.kp, self.vp = inp.k_pool.cuda(), inp.v_pool.cuda()
+        self.bt, self.lens = inp.block_table.cuda(), inp.seq_lens.cuda()
+        self.o = torch.empty(self.q.shape, dtype=torch.bfloat16, device="cuda")
+        lens = inp.seq_lens.numpy().astype(int)
+        self.tokens = int(lens.sum())
+        # visible pairs: row i of sequence s sees L_s - q_len + i + 1 keys
+        pairs = sum(w.q_len * (L - w.q_len) + w.q_len * (w.q_len + 1) // 2 for L in lens)
+        self.flops = 4.0 * w.d * pairs * w.H
+        max_tok = self.bt.shape[1] * w.page_size
+        self.k_out = torch.empty((w.n_seq, w.H, max_tok, w.d), dtype=torch.bfloat16, device="cuda")
+        self.v_out = torch.empty_like(self.k_out)
+        self.gather_bytes = 2.0 * 2 * self.tokens * w.H * w.d * 2      # K and V, read and written
+
+        def step():
+            A.attn_prefill_paged(self.q, self.kp, self.vp, self.bt, self.lens, self.o, w.scale)
+
+        def gather():
+            A.attn_gather_paged(self.kp, self.vp, self.bt, self.lens, self.k_out, self.v_out)
+        self.step = step
+        self.gather = gather
+
+    def describe(self):
+        w = self.w
+        return {"workload": w.name, "sequences": w.n_seq, "heads": w.H, "head_dim": w.d, "page_size": w.page_size,
+                "q_len": w.q_len, "kv_len": [w.l_min, w.l_max], "kv_tokens": self.tokens, "seed": self.seed}
+
+
+class PagedCross:
+    """attn_cross_paged: every 128-row query block over its own page list."""
+
+    def __init__(self, key, seed):
+        import torch
+        from tiled_attention_amd import _lib as A
+        from tiled_attention_amd import workloads as wl
+        self.w = w = wl.WORKLOADS[key]
+        self.seed = seed
+        inp = wl.paged_cross_inputs(w.n_seq, w.H, w.d, w.q_len, w.pool_pages, w.pages_per_block, seed=seed,
+                                    page_size=w.page_size, spare=w.spare_pages)
+        self.q = inp.q.cuda()
+        self.kp, self.vp = inp.k_pool.cuda(), inp.v_pool.cuda()
+        self.table, self.lens = inp.page_table.cuda(), inp.kv_lens.cuda()
+        self.o = torch.empty(self.q.shape, dtype=torch.bfloat16, device="cuda")
+        lens = inp.kv_lens.numpy().astype(int)
+        rows = [min(128, w.q_len - 128 * b) for b in range(lens.shape[1])]
+        self.flops = 4.0 * w.d * w.H * sum(int(lens[s, b]) * rows[b] for s in range(lens.shape[0])
+                                            for b in range(lens.shape[1]))
+
+        def step():
+            A.attn_cross_paged(self.q, self.kp, self.vp, self.table, self.lens, self.o, w.scale)
+        self.step = step
+
+    def describe(self):
+        w = self.w
+        return {"workload": w.name, "sequences": w.n_seq, "heads": w.H, "head_dim": w.d, "page_size": w.page_size,
+                "q_len": w.q_len, "pool_pages": w.pool_pages, "pages_per_query_block": w.pages_per_block,
+                "seed": self.seed}
+
+
 def event_time_ms(step, reps, warmup=3):
     """Average duration of one step from HIP events on the launch stream."""
     import torch
@@ -273,7 +344,8 @@ def main():
     def make(key):
         seed = args.seed if args.seed is not None else wl.default_seed(key)
         w = wl.WORKLOADS[key]
-        return (Paged if w.kind == "paged" else Fp8 if w.kind == "fp8" else Dense)(key, seed)
+        return {"paged": Paged, "fp8": Fp8, "paged_prefill": PagedPrefill, "paged_cross": PagedCross}.get(
+            w.kind, Dense)(key, seed)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -328,7 +400,8 @@ def main():
 
     if not args.only_main:
         others = {}
-        for key, reps in ((1, 200), (3, 20), (4, 20), (5, 20), (6, 20), (7, 20), (8, 10), (9, 20), (10, 20)):
+        for key, reps in ((1, 200), (3, 20), (4, 20), (5, 20), (6, 20), (7, 20), (8, 10), (9, 20), (10, 20),
+                          (11, 20), (12, 20)):
             log(f"bench: workload {key}")
             o = make(key)
             avg, med, mn = event_time_ms(o.step, reps)
@@ -347,10 +420,14 @@ def main():
                     entry.update({"frac_of_blended_peak": round(blended_s / (avg * 1e-3), 4),
                                   "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
                                   "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-                elif o.w.dtype == "f32":
+                elif getattr(o.w, "dtype", "") == "f32" and o.w.kind == "dense":
                     entry["frac_of_fp32_valu_peak"] = round(tf / PEAK_FP32_VALU_TFLOPS, 6)
                 else:
                     entry["frac_of_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+            if isinstance(o, PagedPrefill):
+                g_avg, _, _ = event_time_ms(o.gather, reps)
+                entry["two_stage_gather_ms"] = round(g_avg, 5)
+                entry["two_stage_gather_GBps"] = round(o.gather_bytes / (g_avg * 1e-3) / 1e9, 1)
             others[o.w.name] = entry
             del o
             torch.cuda.empty_cache()

@@ -154,7 +154,7 @@ attn_status attn_quant_fp8_block(const float* x, uint8_t* codes, float* scales,
  *                    never read. Page ids must lie in [0, num_pages): they
  *                    are not checked on the device (caller's contract).
  *   seq_lens       : [S] int32 (device), 1 <= seq_lens[s] <= max_pages*page_size.
- *   page_size must be 16.
+ *   page_size must be 16 for the decode (the gather also takes 64).
  */
 
 /* Bytes of workspace attn_decode_paged uses to split long sequences. */
@@ -178,11 +178,54 @@ attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_p
                               void* stream);
 
 /*
+ * attn_prefill_paged -- causal prefill over a paged KV cache ("Optimizing
+ * Triton kernels ...", Pattern C, its prefix-caching use), with the page
+ * gather fused into the attention's tile loads instead of a separate
+ * gather-then-attend pass.
+ *   The last q_len positions of every sequence are the query rows: row i of
+ *   sequence s sits at position seq_lens[s] - q_len + i and sees the keys at
+ *   positions 0 .. that position (the new rows' own K/V already in the pool).
+ *   q, o : [S, H, q_len, d]; q bf16, o of out_dtype (ATTN_BF16 or ATTN_F32).
+ *   k_pool, v_pool : [num_pages, H, page_size, d] bf16; page_size must be 64
+ *            (one page of one head is one 64-key tile).
+ *   block_table : [S, max_pages] int32 (device), as for attn_decode_paged.
+ *   seq_lens : [S] int32 (device), q_len <= seq_lens[s] <= max_pages * 64.
+ *   max_pages <= 4096 (a list is staged on chip). lse : NULL or [S, H, q_len] fp32.
+ * The device contents (page ids, lengths) are the caller's contract and are
+ * not checked: lengths are clamped to [0, max_pages * 64] and page ids into
+ * [0, num_pages), so other contents give unspecified results but no access
+ * outside the buffers.
+ */
+attn_status attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* seq_lens, void* o,
+                               int S, int H, int q_len, int d, int page_size, int max_pages,
+                               int num_pages, attn_dtype out_dtype, float scale, float* lse,
+                               void* stream);
+
+/*
+ * attn_cross_paged -- block-sparse paged cross-attention ("Optimizing Triton
+ * kernels ...", Pattern C: each query block reads its own set of pages, as in
+ * retrieval). Query block b of sequence s, rows 128b .. 128b + 127 of q[s],
+ * attends with no mask to the first kv_lens[s, b] tokens of the
+ * concatenation of pages page_table[s, b, 0], page_table[s, b, 1], ...
+ *   q, o, pools, page_size (64), max_pages (<= 4096) as for attn_prefill_paged.
+ *   page_table : [S, ceil(q_len / 128), max_pages] int32 (device).
+ *   kv_lens : [S, ceil(q_len / 128)] int32 (device), 0 <= kv_lens <= max_pages * 64;
+ *            a block with no key gets O = 0 and LSE = -inf.
+ * Device contents are handled as for attn_prefill_paged.
+ */
+attn_status attn_cross_paged(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* page_table, const int32_t* kv_lens, void* o,
+                             int S, int H, int q_len, int d, int page_size, int max_pages,
+                             int num_pages, attn_dtype out_dtype, float scale, float* lse,
+                             void* stream);
+
+/*
  * attn_gather_paged -- stage one of the two-stage paged route: a bit copy
  *   k_out[s, h, t, :] = k_pool[block_table[s, t / page_size], h, t % page_size, :]
  * (same for v) for t < seq_lens[s]. k_out, v_out: [S, H, max_pages*page_size, d]
  * of `dtype` (ATTN_BF16 or ATTN_F32, element size only); rows t >= seq_lens[s]
- * are left untouched.
+ * are left untouched. page_size 16 (the decode's pages) or 64 (the prefill's).
  */
 attn_status attn_gather_paged(const void* k_pool, const void* v_pool,
                               const int32_t* block_table, const int32_t* seq_lens,

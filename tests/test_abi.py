@@ -129,6 +129,32 @@ def test_paged_rejects_and_workspace_size():
     assert lib.attn_gather_paged(*bad) == _lib.ATTN_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("name", ["attn_prefill_paged", "attn_cross_paged"])
+def test_paged_prefill_rejects(name):
+    f = getattr(_lib.load(), name)
+    # q, k_pool, v_pool, table, lens, o, S, H, q_len, d, page, max_pages, num_pages, out, scale, lse, stream
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 300, 128, 64, 8, 20, _lib.ATTN_BF16, 0.1, None, None]
+    for i in (0, 1, 2, 3, 4, 5):
+        bad = list(ok); bad[i] = None
+        assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
+    bad = list(ok); bad[10] = 16
+    assert f(*bad) == _lib.ATTN_ERR_UNSUPPORTED          # 16-token pages: the decode's, not these
+    bad = list(ok); bad[11] = 4097
+    assert f(*bad) == _lib.ATTN_ERR_UNSUPPORTED          # list longer than the on-chip staging
+    bad = list(ok); bad[9] = 96
+    assert f(*bad) == _lib.ATTN_ERR_UNSUPPORTED
+    bad = list(ok); bad[8] = 0
+    assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
+    bad = list(ok); bad[13] = _lib.ATTN_FP8_E4M3
+    assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
+    bad = list(ok); bad[3] = FAKE + 2
+    assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
+    bad = list(ok); bad[1] = FAKE_MIS
+    assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
+    bad = list(ok); bad[14] = float("nan")
+    assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
+
+
 def _expected_class(vis, N, m0, m1, n0, n1):
     """EMPTY / PARTIAL / FULL of a tile from the oracle's visibility matrix."""
     rows = [i for i in range(m0, min(m1, N))]

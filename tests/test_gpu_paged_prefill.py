@@ -1,0 +1,153 @@
+"""GPU parity of the fused paged prefill and block-sparse paged
+cross-attention ("Optimizing Triton kernels for custom attention patterns on
+H100", Pattern C) against the oracle, element by element on small ragged
+cases and on sampled rows at the full workload sizes. The pools hold NaN in
+every row no sequence or list owns, so a read past a list shows up."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import LSE_TOL_MFMA, check_close, sample_rows, say, to_np
+from tiled_attention_amd import _lib as A
+from tiled_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(inp, q_len, out_dtype, scale):
+    q = inp.q.cuda()
+    S, H, _, d = q.shape
+    o = torch.full(q.shape, float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full((S, H, q_len), float("nan"), dtype=torch.float32, device="cuda")
+    A.attn_prefill_paged(q, inp.k_pool.cuda(), inp.v_pool.cuda(), inp.block_table.cuda(), inp.seq_lens.cuda(), o,
+                         scale, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# (S, H, q_len, d, l_min, l_max): ragged lengths, q_len from one row to several blocks
+PREFILL = [(3, 2, 1, 128, 1, 200), (2, 3, 100, 64, 100, 700), (4, 2, 300, 128, 300, 1500),
+           (2, 1, 129, 64, 129, 129), (3, 2, 512, 128, 512, 2000), (1, 2, 64, 64, 64, 64),
+           (5, 1, 33, 128, 40, 900)]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_prefill_paged_small_elementwise(case, out):
+    S, H, q_len, d, l_min, l_max = case
+    say(f"paged prefill {case} out={out}")
+    inp = wl.paged_inputs(S, H, d, l_min, l_max, seed=41 + q_len + d, page_size=64, spare=5, q_rows=q_len)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _prefill(inp, q_len, torch.float32 if out == "f32" else torch.bfloat16, scale)
+    ref, ref_lse = oracle.prefill(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
+                                  inp.block_table.numpy(), inp.seq_lens.numpy(), scale, page_size=64)
+    check_close(to_np(o), ref, out == "bf16", what=str(case))
+    assert np.max(np.abs(to_np(lse) - ref_lse)) <= LSE_TOL_MFMA
+
+
+def _cross(inp, out_dtype, scale):
+    q = inp.q.cuda()
+    o = torch.full(q.shape, float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    A.attn_cross_paged(q, inp.k_pool.cuda(), inp.v_pool.cuda(), inp.page_table.cuda(), inp.kv_lens.cuda(), o,
+                       scale, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# (S, H, q_len, d, pool pages, pages per block)
+CROSS = [(2, 2, 300, 64, 9, 4), (1, 3, 128, 128, 40, 17), (3, 1, 1, 128, 5, 1), (2, 2, 700, 128, 64, 40),
+         (1, 1, 257, 64, 3, 3)]
+
+
+@pytest.mark.parametrize("case", CROSS, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_cross_paged_small_elementwise(case, out):
+    S, H, q_len, d, pool, per = case
+    say(f"paged cross {case} out={out}")
+    inp = wl.paged_cross_inputs(S, H, d, q_len, pool, per, seed=43 + q_len, page_size=64, spare=3)
+    if S * (-(-q_len // 128)) > 1:
+        inp.kv_lens[0, -1] = 0                 # one block with no keys: O = 0, LSE = -inf
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _cross(inp, torch.float32 if out == "f32" else torch.bfloat16, scale)
+    ref, ref_lse = oracle.cross(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
+                                inp.page_table.numpy(), inp.kv_lens.numpy(), scale, page_size=64)
+    check_close(to_np(o), ref, out == "bf16", what=str(case))
+    got_lse = to_np(lse)
+    live = np.isfinite(ref_lse)
+    assert np.all(got_lse[~live] == -np.inf)
+    assert np.max(np.abs(got_lse[live] - ref_lse[live])) <= LSE_TOL_MFMA
+
+
+def test_prefill_paged_full_size_sampled():
+    w = wl.WORKLOADS[11]
+    seed = wl.default_seed(11)
+    say(f"{w.name}: generating inputs (seed {seed})")
+    inp = wl.paged_inputs(w.n_seq, w.H, w.d, w.l_min, w.l_max, seed=seed, page_size=w.page_size,
+                          spare=w.spare_pages, q_rows=w.q_len)
+    say(f"{w.name}: running attn_prefill_paged")
+    o, lse = _prefill(inp, w.q_len, torch.bfloat16, w.scale)
+    o32, _ = _prefill(inp, w.q_len, torch.float32, w.scale)
+    assert torch.isfinite(o).all() and torch.isfinite(o32).all()
+    kp, vp = inp.k_pool.float().numpy(), inp.v_pool.float().numpy()
+    table, lens = inp.block_table.numpy(), inp.seq_lens.numpy()
+    for s, h in [(0, 0), (7, 31), (15, 12)]:
+        rows = sample_rows(w.q_len, seed + s)
+        L = int(lens[s])
+        k = oracle.gather(kp, table[s:s + 1], lens[s:s + 1], page_size=64)[0][h]
+        v = oracle.gather(vp, table[s:s + 1], lens[s:s + 1], page_size=64)[0][h]
+        ref, ref_lse = oracle.attention(wl.bf16_to_f64(inp.q[s, h]), k, v, w.scale, "causal", rows=rows,
+                                        q_pos_offset=L - w.q_len)
+        check_close(to_np(o32[s, h][rows]), ref, False, what=f"{w.name} f32 {(s, h)}")
+        check_close(to_np(o[s, h][rows]), ref, True, what=f"{w.name} bf16 {(s, h)}")
+        assert np.max(np.abs(to_np(lse[s, h][rows]) - ref_lse)) <= LSE_TOL_MFMA
+    say(f"{w.name}: sampled rows match")
+
+
+def test_cross_paged_full_size_sampled():
+    w = wl.WORKLOADS[12]
+    seed = wl.default_seed(12)
+    say(f"{w.name}: generating inputs (seed {seed})")
+    inp = wl.paged_cross_inputs(w.n_seq, w.H, w.d, w.q_len, w.pool_pages, w.pages_per_block, seed=seed,
+                                page_size=w.page_size, spare=w.spare_pages)
+    say(f"{w.name}: running attn_cross_paged")
+    o, lse = _cross(inp, torch.bfloat16, w.scale)
+    o32, _ = _cross(inp, torch.float32, w.scale)
+    assert torch.isfinite(o).all() and torch.isfinite(o32).all()
+    kp, vp = inp.k_pool.float().numpy(), inp.v_pool.float().numpy()
+    for s, h, b in [(0, 0, 0), (3, 17, 5), (7, 31, 7)]:
+        rows = [r for r in sample_rows(128, seed + s + b, extra=8) if r < 128]
+        n = int(inp.kv_lens[s, b])
+        k = oracle.listed_keys(kp, inp.page_table[s, b].numpy(), n, 64)[h].astype(np.float64)
+        v = oracle.listed_keys(vp, inp.page_table[s, b].numpy(), n, 64)[h].astype(np.float64)
+        qrows = [128 * b + r for r in rows]
+        ref, ref_lse = oracle.attention(wl.bf16_to_f64(inp.q[s, h]), k, v, w.scale, "none", rows=qrows)
+        check_close(to_np(o32[s, h][qrows]), ref, False, what=f"{w.name} f32 {(s, h, b)}")
+        check_close(to_np(o[s, h][qrows]), ref, True, what=f"{w.name} bf16 {(s, h, b)}")
+        assert np.max(np.abs(to_np(lse[s, h][qrows]) - ref_lse)) <= LSE_TOL_MFMA
+    say(f"{w.name}: sampled rows match")
+
+
+def test_prefill_paged_one_row_matches_decode():
+    """q_len = 1 is a decode: the fused prefill kernel and the split-KV decode agree."""
+    inp = wl.paged_inputs(4, 2, 128, 1, 3000, seed=47, page_size=64, spare=2, q_rows=1)
+    o, _ = _prefill(inp, 1, torch.float32, 1 / math.sqrt(128))
+    ref, _ = oracle.decode(wl.bf16_to_f64(inp.q[:, :, 0]), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
+                           inp.block_table.numpy(), inp.seq_lens.numpy(), 1 / math.sqrt(128), page_size=64)
+    check_close(to_np(o[:, :, 0]), ref, False, what="q_len=1")
+
+
+def test_paged_prefill_rejects():
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    o = torch.full_like(q, 3.0)
+    pool16 = torch.zeros(4, 1, 16, 64, dtype=torch.bfloat16, device="cuda")
+    table = torch.zeros(1, 4, dtype=torch.int32, device="cuda")
+    lens = torch.full((1,), 8, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):            # 16-token pages: unsupported here
+        A.attn_prefill_paged(q, pool16, pool16, table, lens, o, 0.125)
+    torch.cuda.synchronize()
+    assert torch.all(o == 3.0)

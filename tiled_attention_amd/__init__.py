@@ -12,8 +12,11 @@ from ._lib import (  # noqa: F401
     attn_decode_paged_workspace_size,
     attn_decode_paged,
     attn_gather_paged,
+    attn_prefill_paged,
+    attn_cross_paged,
     attn_tile_class,
     attn_k_tile_range,
+    attn_full_tile_range,
     attn_status_str,
     attn_abi_version,
     load,

@@ -30,6 +30,10 @@ _PROTOS = {
     "attn_decode_paged_workspace_size": (_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_decode_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_float, _p, _p, _size, _p]),
+    "attn_prefill_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_float, _p, _p]),
+    "attn_cross_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                  _c_int, _c_int, _c_float, _p, _p]),
     "attn_gather_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_int, _p]),
     "attn_tile_class": (_c_int, [_c_int, _c_int, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
@@ -167,6 +171,27 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, scale, worksp
                                     _ptr(o), S, H, d, page_size, max_pages, num_pages, float(scale), _ptr(lse),
                                     _ptr(workspace), ws_bytes, _stream(stream)))
     return o
+
+
+def _paged_fwd(fn, q, k_pool, v_pool, table, lens, o, scale, lse, stream):
+    _dev(q, k_pool, v_pool, table, lens, o, lse)
+    _require(q.dim() == 4 and o.shape == q.shape, "q, o must be [S, H, q_len, d]")
+    S, H, q_len, d = q.shape
+    num_pages, _, page_size, _ = k_pool.shape
+    max_pages = table.shape[-1]
+    _check(fn(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(table), _ptr(lens), _ptr(o), S, H, q_len, d, page_size,
+              max_pages, num_pages, _dtype_code(o), float(scale), _ptr(lse), _stream(stream)))
+    return o
+
+
+def attn_prefill_paged(q, k_pool, v_pool, block_table, seq_lens, o, scale, lse=None, stream=None):
+    """Causal prefill of the last q_len positions of each paged sequence (64-token pages)."""
+    return _paged_fwd(load().attn_prefill_paged, q, k_pool, v_pool, block_table, seq_lens, o, scale, lse, stream)
+
+
+def attn_cross_paged(q, k_pool, v_pool, page_table, kv_lens, o, scale, lse=None, stream=None):
+    """Block-sparse cross-attention: query block b of sequence s over its own page list."""
+    return _paged_fwd(load().attn_cross_paged, q, k_pool, v_pool, page_table, kv_lens, o, scale, lse, stream)
 
 
 def attn_gather_paged(k_pool, v_pool, block_table, seq_lens, k_out, v_out, stream=None):

@@ -182,13 +182,72 @@ attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_p
   return launched(attn::launch_decode(a, (hipStream_t)stream));
 }
 
+// Shared checks of the two 64-token-page prefill entry points.
+static attn_status paged_fwd(const void* q, const void* k_pool, const void* v_pool, const int32_t* table,
+                             const int32_t* lens, void* o, int S, int H, int q_len, int d, int page_size,
+                             int max_pages, int num_pages, attn_dtype out_dtype, float scale, float* lse,
+                             void* stream, bool causal) {
+  if (!q || !o || !k_pool || !v_pool || !table || !lens) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k_pool) || !aligned16(v_pool)) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)table & 3u) || ((uintptr_t)lens & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
+  if (page_size < 1 || max_pages < 1 || num_pages < 1) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_dims(S, H, q_len, d);
+  if (st != ATTN_OK) return st;
+  const int qb = (q_len + 127) / 128;
+  if ((long long)S * qb * max_pages >= (1LL << 31)) return ATTN_ERR_INVALID_ARG;
+  if (page_size != attn::kPrefillPageSize || max_pages > attn::kPrefillMaxPages) return ATTN_ERR_UNSUPPORTED;
+  attn::PagedFwdArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.o = o;
+  a.lse = lse;
+  a.table = table;
+  a.lens = lens;
+  a.S = S;
+  a.H = H;
+  a.q_len = q_len;
+  a.d = d;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.table_stride_s = causal ? max_pages : qb * max_pages;
+  a.table_stride_b = causal ? 0 : max_pages;
+  a.lens_stride_s = causal ? 1 : qb;
+  a.lens_stride_b = causal ? 0 : 1;
+  a.causal = causal;
+  a.out_f32 = out_dtype == ATTN_F32;
+  a.scale = scale;
+  return launched(attn::launch_fwd_paged(a, (hipStream_t)stream));
+}
+
+attn_status attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, void* o, int S, int H, int q_len, int d, int page_size,
+                               int max_pages, int num_pages, attn_dtype out_dtype, float scale, float* lse,
+                               void* stream) {
+  return paged_fwd(q, k_pool, v_pool, block_table, seq_lens, o, S, H, q_len, d, page_size, max_pages, num_pages,
+                   out_dtype, scale, lse, stream, true);
+}
+
+attn_status attn_cross_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* page_table,
+                             const int32_t* kv_lens, void* o, int S, int H, int q_len, int d, int page_size,
+                             int max_pages, int num_pages, attn_dtype out_dtype, float scale, float* lse,
+                             void* stream) {
+  return paged_fwd(q, k_pool, v_pool, page_table, kv_lens, o, S, H, q_len, d, page_size, max_pages, num_pages,
+                   out_dtype, scale, lse, stream, false);
+}
+
 attn_status attn_gather_paged(const void* k_pool, const void* v_pool, const int32_t* block_table,
                               const int32_t* seq_lens, void* k_out, void* v_out, int S, int H, int d,
                               int page_size, int max_pages, int num_pages, attn_dtype dtype, void* stream) {
   if (!k_out || !v_out) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(k_out) || !aligned16(v_out)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_INVALID_ARG;
-  attn_status st = check_paged(k_pool, v_pool, block_table, seq_lens, S, H, d, page_size, max_pages, num_pages);
+  // the copy takes the decode's 16-token pages and the prefill's 64-token pages
+  attn_status st = check_paged(k_pool, v_pool, block_table, seq_lens, S, H, d, page_size == 64 ? 16 : page_size,
+                               max_pages, num_pages);
   if (st != ATTN_OK) return st;
   if ((long long)S * H * max_pages * page_size >= (1LL << 31)) return ATTN_ERR_INVALID_ARG;
   attn::GatherArgs a{};
@@ -203,6 +262,7 @@ attn_status attn_gather_paged(const void* k_pool, const void* v_pool, const int3
   a.d = d;
   a.max_pages = max_pages;
   a.elem_bytes = dtype == ATTN_F32 ? 4 : 2;
+  a.page_size = page_size;
   return launched(attn::launch_gather(a, (hipStream_t)stream));
 }
 

@@ -53,6 +53,12 @@
 //  * Causal and prefix-LM: a workgroup takes Q tiles t and T-1-t so all carry
 //    about equal work; workgroup ids are mapped so that a head's tiles share
 //    an XCD (its L2).
+//  * Paged K/V ("Optimizing Triton kernels ...", Pattern C, fused instead of
+//    gather-then-attend): with 64-token pages of a [pages, H, 64, d] pool one
+//    page of one head is exactly one K (or V) tile, contiguous, so the same
+//    LDS DMA fetches it from its page's address. A Q tile's page list is
+//    staged in LDS once; each issue reads its page id from there and clips
+//    the descriptor at the list's last valid token (later rows load as zeros).
 #include <type_traits>
 #include <utility>
 
@@ -116,6 +122,13 @@ struct Params {
   const float* k_scale;
   const int32_t* doc;
   int N, mask, window, nd, n_qtiles, units_per_bh, units, pair, nsb;
+  // paged K/V: k, v are [pool pages, H, 64, d] pools; (sequence s, query
+  // block b) reads the page list pg_table + s * pg_stride_s + b * pg_stride_b
+  // and its length pg_lens[s * len_stride_s + b * len_stride_b] (the sequence
+  // length when pg_causal, else the number of keys)
+  const int32_t* pg_table;
+  const int32_t* pg_lens;
+  int H, pg_stride_s, pg_stride_b, len_stride_s, len_stride_b, pg_max, pg_pool, pg_causal;
   float scale_log2;
 };
 
@@ -175,8 +188,9 @@ struct TileStream {
   }
 };
 
-template <int D, bool FP8, bool OUT_F32>
+template <int D, bool FP8, bool OUT_F32, bool PG>
 struct QTile {
+  static_assert(!(PG && FP8), "paged K/V is bf16");
   using C = Cfg<D, FP8>;
   static constexpr int KROW = C::KROW, VROW = C::VROW, QK_STEPS = C::QK_STEPS, DE = C::DE;
   static constexpr int KLD = C::KLD, VLD = C::VLD, L = KLD + VLD, NS = C::NS, U = C::U;
@@ -199,6 +213,10 @@ struct QTile {
   int vread[DE];
   uint32_t lds_k, lds_v;    // this wave's DMA destinations in slot 0 (K, V)
   TileStream ks, vs;
+  // paged mode: pools, page ids in LDS, valid keys of the list, next tile of each stream
+  uint64_t pool_k, pool_v;
+  const int* pg_ids;
+  int pg_h, pg_len, k_next, v_next;
 
   float m_ref;              // reference (log2 units) of the exponentials; -inf: none yet
   float m_use;              // m_ref, or 0 while it is -inf
@@ -227,9 +245,37 @@ struct QTile {
     head = (size_t)bh * N;
 
     const int wr0 = min(wrow0, N - 1), wr1 = min(wrow0 + 31, N - 1);
-    const RowSpans sp = row_spans(p.mask, p.window, p.doc, p.nd, N, m0, m1 - 1, wr0, wr1, qsrc);
-    touched_tiles(sp.tile_first, sp.tile_last, BN, &t_lo, &NK);
-    NK -= t_lo;
+    RowSpans sp;
+    if constexpr (PG) {
+      // keys [0, hi(row)]: causal prefill rows sit at positions len - N + row
+      const int s = bh / p.H;
+      pg_h = bh - s * p.H;
+      const int32_t* list = p.pg_table + (size_t)s * p.pg_stride_s + (size_t)qt * p.pg_stride_b;
+      pg_len = min(max(p.pg_lens[s * p.len_stride_s + qt * p.len_stride_b], 0), p.pg_max * BN);
+      const int pos0 = pg_len - N;
+      auto span = [&](int r) -> KeySpan { return {0, p.pg_causal ? min(pg_len - 1, pos0 + r) : pg_len - 1}; };
+      sp.lane = span(qsrc);
+      sp.wave_first = span(wr0);
+      sp.wave_last = span(wr1);
+      sp.tile_first = span(m0);
+      sp.tile_last = span(m1 - 1);
+      t_lo = 0;
+      NK = sp.tile_last.hi >= 0 ? sp.tile_last.hi / BN + 1 : 0;
+      // stage the page ids of the tiles this Q tile visits (clamped into the
+      // pool); NK <= pg_max <= kPrefillMaxPages
+      int* ids = (int*)(smem + C::LDS);
+      for (int i = tid; i < NK; i += NT) ids[i] = min(max(list[i], 0), p.pg_pool - 1);
+      __syncthreads();
+      pg_ids = ids;
+      pool_k = (uint64_t)(uintptr_t)p.k;
+      pool_v = (uint64_t)(uintptr_t)p.v;
+      k_next = 0;
+      v_next = 0;
+    } else {
+      sp = row_spans(p.mask, p.window, p.doc, p.nd, N, m0, m1 - 1, wr0, wr1, qsrc);
+      touched_tiles(sp.tile_first, sp.tile_last, BN, &t_lo, &NK);
+      NK -= t_lo;
+    }
     // opaque to the optimizer: bounds it can reason about (NK >= 1, t_lo = 0
     // for causal masks) let it restructure the tile loop of the fp8 kernels
     // in a way that overflows the VGPRs
@@ -278,8 +324,8 @@ struct QTile {
     const uint32_t lds0 = lds_addr(smem);
     lds_k = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
     lds_v = __builtin_amdgcn_readfirstlane(lds0 + NS * C::K_SLOT + wave * 1024);
-    const uint64_t kb = (uint64_t)(uintptr_t)p.k + (head + (size_t)t_lo * BN) * KROW;
-    const uint64_t vb = (uint64_t)(uintptr_t)p.v + (head + (size_t)t_lo * BN) * VROW;
+    const uint64_t kb = PG ? 0 : (uint64_t)(uintptr_t)p.k + (head + (size_t)t_lo * BN) * KROW;
+    const uint64_t vb = PG ? 0 : (uint64_t)(uintptr_t)p.v + (head + (size_t)t_lo * BN) * VROW;
     const int rem = N - t_lo * BN;
     ks.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kb >> 32)) << 32) |
               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kb);
@@ -314,8 +360,26 @@ struct QTile {
   }
 
   // DMA of the next K tile into ring slot SLOT; the stream moves one tile on.
+  // descriptor of paged tile j (page pg_ids[j] of this head), clipped at the list's length
+  __device__ __forceinline__ i32x4 page_rsrc(uint64_t pool, int j, int slot_bytes, int row_bytes) const {
+    const int jc = max(min(j, NK - 1), 0);
+    const int pid = __builtin_amdgcn_readfirstlane(pg_ids[jc]);
+    const uint64_t base = pool + ((uint64_t)pid * p.H + pg_h) * (uint64_t)slot_bytes;
+    const int rows = min(max(pg_len - j * BN, 0), BN);
+    // every word is wave-uniform; readfirstlane keeps the descriptor in SGPRs
+    return (i32x4){__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                   __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32)),
+                   __builtin_amdgcn_readfirstlane(rows * row_bytes), kBufferFlags};
+  }
+
   template <int SLOT>
   __device__ __forceinline__ void issue_k() {
+    if constexpr (PG) {
+      const i32x4 rs = page_rsrc(pool_k, k_next++, C::K_SLOT, KROW);
+#pragma unroll
+      for (int u = 0; u < KLD; ++u) dma16(lds_k + SLOT * C::K_SLOT + u * NW * 1024, kdma[u], rs);
+      return;
+    }
     const i32x4 rs = ks.rsrc();
 #pragma unroll
     for (int u = 0; u < KLD; ++u) dma16(lds_k + SLOT * C::K_SLOT + u * NW * 1024, kdma[u], rs);
@@ -324,6 +388,12 @@ struct QTile {
   }
   template <int SLOT>
   __device__ __forceinline__ void issue_v() {
+    if constexpr (PG) {
+      const i32x4 rs = page_rsrc(pool_v, v_next++, C::V_SLOT, VROW);
+#pragma unroll
+      for (int u = 0; u < VLD; ++u) dma16(lds_v + SLOT * C::V_SLOT + u * NW * 1024, vdma[u], rs);
+      return;
+    }
     const i32x4 rs = vs.rsrc();
 #pragma unroll
     for (int u = 0; u < VLD; ++u) dma16(lds_v + SLOT * C::V_SLOT + u * NW * 1024, vdma[u], rs);
@@ -586,9 +656,9 @@ struct QTile {
   }
 };
 
-template <int D, bool FP8, bool OUT_F32>
+template <int D, bool FP8, bool OUT_F32, bool PG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8>::LDS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8>::LDS + (PG ? 4 * kPrefillMaxPages : 0)];
   const int u = xcd_unit(blockIdx.x, gridDim.x);
   if (u >= p.units) return;
   const int bh = u / p.units_per_bh;
@@ -597,14 +667,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // the Q loads, so the two latencies overlap)
   const int ta = w, tb = p.n_qtiles - 1 - w;
   {
-    QTile<D, FP8, OUT_F32> a(p, smem, bh, tb);
+    QTile<D, FP8, OUT_F32, PG> a(p, smem, bh, tb);
     a.start_stream();
     a.load_q();
     a.loop();
     a.epilogue();
   }
   if (p.pair && ta != tb) {
-    QTile<D, FP8, OUT_F32> b(p, smem, bh, ta);
+    QTile<D, FP8, OUT_F32, PG> b(p, smem, bh, ta);
     b.start_stream();
     b.load_q();
     b.loop();
@@ -612,30 +682,57 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
+Params base_params(const void* q, const void* k, const void* v, void* o, float* lse, int N, float scale) {
+  Params p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.N = N;
+  p.n_qtiles = (N + BM - 1) / BM;
+  p.nsb = (N + 127) / 128;
+  p.scale_log2 = scale * kLog2e;
+  return p;
+}
+
+template <int D, bool FP8, bool OUT_F32, bool PG>
+hipError_t launch_p(Params& p, int BH, hipStream_t stream) {
+  p.units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
+  p.units = BH * p.units_per_bh;
+  const int grid = round_up8(p.units);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32, PG>), dim3(grid), dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D, bool FP8, bool OUT_F32>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  Params p;
-  p.q = a.q;
-  p.k = a.k;
-  p.v = a.v;
-  p.o = a.o;
-  p.lse = a.lse;
+  Params p = base_params(a.q, a.k, a.v, a.o, a.lse, a.N, a.scale);
   p.q_scale = a.q_scale;
   p.k_scale = a.k_scale;
   p.doc = a.doc;
-  p.N = a.N;
   p.mask = a.mask;
   p.window = a.window;
   p.nd = a.num_docs;
-  p.n_qtiles = (a.N + BM - 1) / BM;
   p.pair = (a.mask == MASK_CAUSAL || a.mask == MASK_PREFIX_LM) ? 1 : 0;
-  p.units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
-  p.units = a.BH * p.units_per_bh;
-  p.nsb = (a.N + 127) / 128;
-  p.scale_log2 = a.scale * kLog2e;
-  const int grid = round_up8(p.units);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32>), dim3(grid), dim3(NT), 0, stream, p);
-  return hipGetLastError();
+  return launch_p<D, FP8, OUT_F32, false>(p, a.BH, stream);
+}
+
+template <int D, bool OUT_F32>
+hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
+  Params p = base_params(a.q, a.k_pool, a.v_pool, a.o, a.lse, a.q_len, a.scale);
+  p.pg_table = a.table;
+  p.pg_lens = a.lens;
+  p.H = a.H;
+  p.pg_stride_s = a.table_stride_s;
+  p.pg_stride_b = a.table_stride_b;
+  p.len_stride_s = a.lens_stride_s;
+  p.len_stride_b = a.lens_stride_b;
+  p.pg_max = a.max_pages;
+  p.pg_pool = a.num_pages;
+  p.pg_causal = a.causal ? 1 : 0;
+  p.pair = p.pg_causal;
+  return launch_p<D, false, OUT_F32, true>(p, a.S * a.H, stream);
 }
 
 }  // namespace
@@ -648,6 +745,11 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t stream) {
     return a.d == 64 ? launch_t<64, false, true>(a, stream) : launch_t<128, false, true>(a, stream);
   }
   return a.d == 64 ? launch_t<64, false, false>(a, stream) : launch_t<128, false, false>(a, stream);
+}
+
+hipError_t launch_fwd_paged(const PagedFwdArgs& a, hipStream_t stream) {
+  if (a.out_f32) return a.d == 64 ? launch_pg<64, true>(a, stream) : launch_pg<128, true>(a, stream);
+  return a.d == 64 ? launch_pg<64, false>(a, stream) : launch_pg<128, false>(a, stream);
 }
 
 }  // namespace attn

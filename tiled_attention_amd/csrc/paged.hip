@@ -247,9 +247,10 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecParams p) {
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int slot = blockIdx.x;
   const int s = blockIdx.y;
+  const int page = a.page_size;
   const int len = a.seq_lens[s];
-  if (slot * PAGE >= len) return;
-  const int rows = min(PAGE, len - slot * PAGE);
+  if (slot * page >= len) return;
+  const int rows = min(page, len - slot * page);
   const int pid = a.block_table[(size_t)s * a.max_pages + slot];
   const int row_chunks = a.d * a.elem_bytes / 16;
   const int per_head = rows * row_chunks;
@@ -260,8 +261,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     const int rem = c - h * per_head;
     const int r = rem / row_chunks;
     const int col = rem - r * row_chunks;
-    const size_t src = (((size_t)pid * a.H + h) * PAGE + r) * row_bytes + (size_t)col * 16;
-    const size_t dst = (((size_t)s * a.H + h) * ((size_t)a.max_pages * PAGE) + (size_t)slot * PAGE + r) * row_bytes +
+    const size_t src = (((size_t)pid * a.H + h) * page + r) * row_bytes + (size_t)col * 16;
+    const size_t dst = (((size_t)s * a.H + h) * ((size_t)a.max_pages * page) + (size_t)slot * page + r) * row_bytes +
                        (size_t)col * 16;
     *(uint4*)((char*)a.k_out + dst) = *(const uint4*)((const char*)a.k_pool + src);
     *(uint4*)((char*)a.v_out + dst) = *(const uint4*)((const char*)a.v_pool + src);

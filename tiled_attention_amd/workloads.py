@@ -17,10 +17,16 @@ Recipe (all draws from ``numpy.random.default_rng(seed)``):
   With outliers, then three masks ``random(shape) < p`` (for Q, K, V in that
   order) scale the chosen entries by ``outlier_scale``.
 * paged: the sequence lengths ``integers(l_min, l_max, endpoint=True)``, then
-  Q [S, H, d], then per sequence K_s and V_s [H, L_s, d], then a permutation
+  Q [S, H, d] (or [S, H, q_len, d] for a prefill of the last q_len
+  positions), then per sequence K_s and V_s [H, L_s, d], then a permutation
   of the P = sum ceil(L_s/16) + spare page ids, handed out in (sequence, slot)
   order. Unused rows of last pages and spare pages hold NaN; block-table
   entries past a sequence's last page hold -1.
+* paged cross-attention: Q [S, H, q_len, d], the K pool, the V pool, then for
+  each (sequence, 128-row query block) ``choice(pool_pages, pages_per_block,
+  replace=False)`` and a cut ``integers(0, page_size)`` of tokens dropped from
+  the end of its list; spare pages past the pool hold NaN, and no list names
+  them.
 * documents: document lengths ``integers(l_min, l_max, endpoint=True)`` from
   ``numpy.random.default_rng([seed, 1])`` (a stream apart from Q, K, V), drawn
   until they cover N; the last document is cut at N. The offsets are the
@@ -57,6 +63,9 @@ class Workload:
     outlier_p: float = 0.0
     outlier_scale: float = 1.0
     qk_block: int = 128
+    q_len: int = 0                 # paged prefill / cross: query rows per sequence
+    pool_pages: int = 0            # paged cross: pages in the pool
+    pages_per_block: int = 0       # paged cross: pages each query block lists
     extra: dict = field(default_factory=dict)
 
     @property
@@ -89,6 +98,13 @@ WORKLOADS = {
     9: Workload(9, "prefix_lm2048_bf16_b2_h16_n8192_d128", "dense", B=2, H=16, N=8192, d=128,
                 mask="prefix_lm", window=2048),
     10: Workload(10, "dense_bf16_b1_h16_n16384_d128", "dense", B=1, H=16, N=16384, d=128, mask="none"),
+    # paged K/V with 64-token pages ("Optimizing Triton kernels ...", Pattern
+    # C): the last 512 positions of 16 cached sequences of 1K..8K tokens, and
+    # 8 x 8 query blocks each reading 32 pages picked from a 1024-page pool
+    11: Workload(11, "paged_prefill_bf16_s16_h32_d128_p64_q512_l1024to8192", "paged_prefill", H=32, d=128,
+                 n_seq=16, l_min=1024, l_max=8192, page_size=64, q_len=512),
+    12: Workload(12, "paged_cross_bf16_s8_h32_d128_p64_q1024_32of1024pages", "paged_cross", H=32, d=128,
+                 n_seq=8, page_size=64, q_len=1024, pool_pages=1024, pages_per_block=32, spare_pages=16),
 }
 
 
