@@ -129,8 +129,19 @@ struct Params {
   const int32_t* pg_table;
   const int32_t* pg_lens;
   int H, pg_stride_s, pg_stride_b, len_stride_s, len_stride_b, pg_max, pg_pool, pg_causal;
+  // heaviest-first dispatch (order != ORDER_NONE): units come in `groups`
+  // groups of `per_group` equal-cost units
+  int order, groups, per_group, n_qb;
   float scale_log2;
 };
+
+enum UnitOrder {
+  ORDER_NONE = 0,    // unit u -> (bh, w) = (u / units_per_bh, u % units_per_bh), XCD-grouped
+  ORDER_DOC = 1,     // groups = Q tiles, costed by the keys their documents span; per group: the heads
+  ORDER_SEQ = 2,     // groups = sequences of a paged prefill, costed by length; per group: heads x units
+  ORDER_BLOCK = 3    // groups = (sequence, query block) lists of a paged cross-attention, costed by length
+};
+constexpr int kOrderMaxDocs = 8192;  // document offsets staged in LDS for the costing
 
 __device__ __forceinline__ float half_swap_max(float x) {
   // max over lane l and lane l^32
@@ -537,6 +548,12 @@ struct QTile {
       asm volatile("" : "+v"(c));
       c_next = tile_scale(i + 1);
     }
+    // refill the slots freed at this step's sync_tiles. A ring of 2 or 3
+    // slots is refilled at once, so the tiles have a whole step to land
+    // before the next step waits for them; a 4-slot ring has slack to spare
+    // and refills after the MFMA block, where a stall on the texture-address
+    // queue overlaps the MFMAs in flight.
+    if constexpr (kEarlyRefill) refill<PH>();
     if ((unsigned)(i - f_lo) >= (unsigned)(f_hi - f_lo)) mask<B>(i);
     // unconditional, so the block has no branch: for i + 1 == NK the slot
     // holds a tile past the band whose scores are never used
@@ -555,8 +572,12 @@ struct QTile {
     // (before P V of the tile, which the next step issues)
     if (__builtin_expect(__any(!(psum <= limit)), 0)) rebase<B>(c, psum);
     l_run += psum;
-    // refill the slots freed at this step's sync_tiles; issued last, so a
-    // stall on the texture-address queue overlaps the MFMAs in flight
+    if constexpr (!kEarlyRefill) refill<PH>();
+  }
+
+  static constexpr bool kEarlyRefill = NS <= 3;
+  template <int PH>
+  __device__ __forceinline__ void refill() {
     issue_k<PH % NS>();                // K_{i+NS} into K_i's slot
     issue_v<(PH + NS - 2) % NS>();     // V_{i+NS-2} into V_{i-2}'s slot
   }
@@ -656,13 +677,94 @@ struct QTile {
   }
 };
 
+// Last document d in [0, nd) whose start offs[d] is <= x (offs in LDS).
+__device__ __forceinline__ int lds_doc_of(const int* offs, int nd, int x) {
+  int lo = 0, hi = nd - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Heaviest-first dispatch. Workgroups are handed out in id order as slots
+// free up, so giving the lowest ids to the costliest units makes that
+// greedy dispatch longest-first. Every workgroup costs all groups (one per
+// thread, groups <= NT), ranks them in LDS (cost descending, then index) and
+// takes the group of rank u / per_group. Uses the LDS before any tile lands.
+__device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* bh, int* w) {
+  int* cost = (int*)smem;
+  int* order = cost + NT;
+  int* offs = order + NT;
+  const int tid = threadIdx.x;
+  const int G = p.groups;
+  if (p.order == ORDER_DOC) {
+    for (int i = tid; i <= p.nd; i += NT) offs[i] = p.doc[i];
+    __syncthreads();
+  }
+  if (tid < G) {
+    int c;
+    if (p.order == ORDER_DOC) {
+      // keys touched by Q tile tid: from the first row's document start to the
+      // last row's document end (or the last row itself when causal)
+      const int m0 = tid * BM, m1 = min(m0 + BM, p.N);
+      const bool causal = p.mask == MASK_DOCUMENT_CAUSAL;
+      int d = lds_doc_of(offs, p.nd, m0);
+      const KeySpan f = doc_span(causal, offs[d], offs[d + 1], p.N, m0);
+      d = lds_doc_of(offs, p.nd, m1 - 1);
+      const KeySpan l = doc_span(causal, offs[d], offs[d + 1], p.N, m1 - 1);
+      c = l.hi / BN - f.lo / BN + 1;
+    } else {
+      c = min(max(p.pg_lens[tid], 0), p.pg_max * BN);
+    }
+    cost[tid] = c;
+  }
+  __syncthreads();
+  if (tid < G) {
+    const int c = cost[tid];
+    int r = 0;
+    for (int g = 0; g < G; ++g) {
+      const int cg = cost[g];
+      r += (cg > c || (cg == c && g < tid)) ? 1 : 0;
+    }
+    order[r] = tid;
+  }
+  __syncthreads();
+  const int grp = order[u / p.per_group];
+  const int sub = u - (u / p.per_group) * p.per_group;
+  __syncthreads();  // the LDS is the ring's from here on
+  if (p.order == ORDER_DOC) {             // group = Q tile, sub = head
+    *bh = sub;
+    *w = p.n_qtiles - 1 - grp;
+  } else if (p.order == ORDER_SEQ) {      // group = sequence, sub = (head, unit)
+    *bh = grp * p.H + sub / p.units_per_bh;
+    *w = sub - (sub / p.units_per_bh) * p.units_per_bh;
+  } else {                                // group = (sequence, query block), sub = head
+    *bh = (grp / p.n_qb) * p.H + sub;
+    *w = p.n_qtiles - 1 - (grp - (grp / p.n_qb) * p.n_qb);
+  }
+}
+
 template <int D, bool FP8, bool OUT_F32, bool PG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8>::LDS + (PG ? 4 * kPrefillMaxPages : 0)];
-  const int u = xcd_unit(blockIdx.x, gridDim.x);
-  if (u >= p.units) return;
-  const int bh = u / p.units_per_bh;
-  const int w = u - bh * p.units_per_bh;
+  int bh, w;
+  if (p.order != ORDER_NONE) {
+    // ranks follow workgroup ids (the dispatch order); each XCD takes every 8th
+    const int u = blockIdx.x;
+    if (u >= p.units) return;
+    ordered_unit(p, smem, u, &bh, &w);
+  } else {
+    const int u = xcd_unit(blockIdx.x, gridDim.x);
+    if (u >= p.units) return;
+    bh = u / p.units_per_bh;
+    w = u - bh * p.units_per_bh;
+  }
+  bh = __builtin_amdgcn_readfirstlane(bh);
+  w = __builtin_amdgcn_readfirstlane(w);
   // the longer Q tile first (its tile stream's first DMAs are issued before
   // the Q loads, so the two latencies overlap)
   const int ta = w, tb = p.n_qtiles - 1 - w;
@@ -715,6 +817,11 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.window = a.window;
   p.nd = a.num_docs;
   p.pair = (a.mask == MASK_CAUSAL || a.mask == MASK_PREFIX_LM) ? 1 : 0;
+  if (is_document(a.mask) && p.n_qtiles <= NT && a.num_docs + 1 <= kOrderMaxDocs) {
+    p.order = ORDER_DOC;
+    p.groups = p.n_qtiles;
+    p.per_group = a.BH;
+  }
   return launch_p<D, FP8, OUT_F32, false>(p, a.BH, stream);
 }
 
@@ -732,6 +839,17 @@ hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
   p.pg_pool = a.num_pages;
   p.pg_causal = a.causal ? 1 : 0;
   p.pair = p.pg_causal;
+  p.n_qb = p.n_qtiles;
+  const int units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
+  if (a.causal && a.S <= NT) {
+    p.order = ORDER_SEQ;
+    p.groups = a.S;
+    p.per_group = a.H * units_per_bh;
+  } else if (!a.causal && a.S * p.n_qtiles <= NT) {
+    p.order = ORDER_BLOCK;
+    p.groups = a.S * p.n_qtiles;
+    p.per_group = a.H;
+  }
   return launch_p<D, false, OUT_F32, true>(p, a.S * a.H, stream);
 }
 
