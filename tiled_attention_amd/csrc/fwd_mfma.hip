@@ -131,15 +131,14 @@ struct Params {
   int H, pg_stride_s, pg_stride_b, len_stride_s, len_stride_b, pg_max, pg_pool, pg_causal;
   // heaviest-first dispatch (order != ORDER_NONE): units come in `groups`
   // groups of `per_group` equal-cost units
-  int order, groups, per_group, n_qb;
+  int order, groups, per_group;
   float scale_log2;
 };
 
 enum UnitOrder {
   ORDER_NONE = 0,    // unit u -> (bh, w) = (u / units_per_bh, u % units_per_bh), XCD-grouped
   ORDER_DOC = 1,     // groups = Q tiles, costed by the keys their documents span; per group: the heads
-  ORDER_SEQ = 2,     // groups = sequences of a paged prefill, costed by length; per group: heads x units
-  ORDER_BLOCK = 3    // groups = (sequence, query block) lists of a paged cross-attention, costed by length
+  ORDER_SEQ = 2      // groups = sequences of a paged prefill, costed by length; per group: heads x units
 };
 constexpr int kOrderMaxDocs = 8192;  // document offsets staged in LDS for the costing
 
@@ -739,12 +738,9 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
   if (p.order == ORDER_DOC) {             // group = Q tile, sub = head
     *bh = sub;
     *w = p.n_qtiles - 1 - grp;
-  } else if (p.order == ORDER_SEQ) {      // group = sequence, sub = (head, unit)
+  } else {                                // ORDER_SEQ: group = sequence, sub = (head, unit)
     *bh = grp * p.H + sub / p.units_per_bh;
     *w = sub - (sub / p.units_per_bh) * p.units_per_bh;
-  } else {                                // group = (sequence, query block), sub = head
-    *bh = (grp / p.n_qb) * p.H + sub;
-    *w = p.n_qtiles - 1 - (grp - (grp / p.n_qb) * p.n_qb);
   }
 }
 
@@ -839,16 +835,14 @@ hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
   p.pg_pool = a.num_pages;
   p.pg_causal = a.causal ? 1 : 0;
   p.pair = p.pg_causal;
-  p.n_qb = p.n_qtiles;
   const int units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
+  // cross-attention lists keep the natural order: ranking them (by length)
+  // measured slower with lists of about equal length, since a list's heads
+  // then run side by side instead of each head's blocks sharing an XCD
   if (a.causal && a.S <= NT) {
     p.order = ORDER_SEQ;
     p.groups = a.S;
     p.per_group = a.H * units_per_bh;
-  } else if (!a.causal && a.S * p.n_qtiles <= NT) {
-    p.order = ORDER_BLOCK;
-    p.groups = a.S * p.n_qtiles;
-    p.per_group = a.H;
   }
   return launch_p<D, false, OUT_F32, true>(p, a.S * a.H, stream);
 }
