@@ -37,12 +37,12 @@ from .attention import visible, attention, probabilities, visible_pair_count
 from .recurrence import tiled_attention, partial_state, merge_partials, split_attention
 from .paged import gather, decode, prefill, cross, listed_keys
 from .fp8 import (E4M3_MAX, e4m3_value, e4m3_table, e4m3_encode, quantize_blocks,
-                  dequantize_blocks)
+                  dequantize_blocks, pow2_scale)
 
 __all__ = [
     "visible", "attention", "probabilities", "visible_pair_count",
     "tiled_attention", "partial_state", "merge_partials", "split_attention",
     "gather", "decode", "prefill", "cross", "listed_keys",
     "E4M3_MAX", "e4m3_value", "e4m3_table", "e4m3_encode", "quantize_blocks",
-    "dequantize_blocks",
+    "dequantize_blocks", "pow2_scale",
 ]

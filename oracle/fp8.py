@@ -71,9 +71,24 @@ def e4m3_encode(y):
     return code.astype(np.uint8)
 
 
-def quantize_blocks(x, block=128):
+def pow2_scale(amax):
+    """Smallest power of two s with amax / s <= 448 (exactly: 448 * s / 2 <
+    amax <= 448 * s), exponent clamped to >= -127; 1 for amax = 0. Computed on
+    the exact binary mantissa of amax: amax = m * 2^e, m in [0.5, 1), and
+    448 = 0.875 * 2^9, so the exponent is e - 9 when m <= 0.875, else e - 8."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, e = np.frexp(amax)
+    k = np.where(m <= 0.875, e - 9, e - 8)
+    k = np.maximum(k, -127)
+    return np.where(amax == 0, 1.0, np.ldexp(1.0, k)).astype(np.float32)
+
+
+def quantize_blocks(x, block=128, pow2=False):
     """Per-block fp8 quantisation of x [..., N, d] (fp32).
 
+    Scale per block: absmax / 448 in fp32 ("FlashAttention-3 ...", "FP8 Block
+    Quantization"), or with pow2 the power of two just above it, so that the
+    scale is an exact power of two a matrix core can apply as an exponent.
     Returns (codes uint8 [..., N, d], scales fp32 [..., ceil(N/block)]).
     """
     x = np.asarray(x, dtype=np.float32)
@@ -84,8 +99,11 @@ def quantize_blocks(x, block=128):
     for b in range(nb):
         blk = x[..., b * block:(b + 1) * block, :]
         amax = np.abs(blk).max(axis=(-2, -1)).astype(np.float32)
-        s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-        s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+        if pow2:
+            s = pow2_scale(amax)
+        else:
+            s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+            s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
         y = (blk / s[..., None, None]).astype(np.float32)
         codes[..., b * block:(b + 1) * block, :] = e4m3_encode(y)
         scales[..., b] = s

@@ -380,3 +380,42 @@ def test_block_quantisation_properties():
     half_ulp = 0.5 * 2.0 ** (e - 3)
     assert np.all(np.abs(x - xhat) <= half_ulp * s * (1 + 1e-5) + 1e-30)
     assert np.all(np.abs(xhat) <= 448.0 * s + 1e-30)
+
+
+def test_power_of_two_block_scales():
+    """pow2 scales: exact powers of two with 224 < absmax / s <= 448 (checked by
+    exact integer-exponent arithmetic, independent of the frexp route), 1 for a
+    zero block; where absmax / 448 is itself a power of two both quantisers
+    agree; dequantisation stays within half an E4M3 step times the scale."""
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((2, 3, 300, 16)).astype(np.float32) * np.float32(3.0)
+    x[0, 1, 128:256] = 0.0
+    x[1, 2, 0:128] *= np.float32(1e-30)
+    codes, s = oracle.quantize_blocks(x, pow2=True)
+    amax = np.abs(x.reshape(2, 3, -1, 16)).reshape(2, 3, -1)
+    for b in range(3):
+        for h in range(2):
+            for hh in range(3):
+                sc = float(s[h, hh, b])
+                m, e = math.frexp(sc)
+                assert m == 0.5                               # a power of two
+                a = float(np.abs(x[h, hh, 128 * b:128 * b + 128]).max())
+                if a == 0:
+                    assert sc == 1.0
+                else:
+                    assert 224.0 * sc < a <= 448.0 * sc or sc == 2.0 ** -127
+    assert oracle.pow2_scale(np.float32(448.0)) == 1.0
+    assert oracle.pow2_scale(np.float32(448.0 * 2 ** -5)) == 2.0 ** -5
+    assert oracle.pow2_scale(np.float32(np.nextafter(np.float32(448.0), np.float32(1e9)))) == 2.0
+    assert oracle.pow2_scale(np.float32(224.0)) == 0.5
+    assert oracle.pow2_scale(np.float32(np.nextafter(np.float32(224.0), np.float32(1e9)))) == 1.0
+    y = np.full((1, 1, 128, 4), 448.0 * 2 ** -3, dtype=np.float32)
+    y[0, 0, 5, 2] = 1.0
+    c1, s1 = oracle.quantize_blocks(y)
+    c2, s2 = oracle.quantize_blocks(y, pow2=True)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    xh = oracle.dequantize_blocks(codes, s)
+    step = np.where(np.abs(xh) >= 2.0 ** -6 * np.repeat(s, 128, axis=-1)[..., :300, None],
+                    np.exp2(np.floor(np.log2(np.maximum(np.abs(xh), 1e-300))) - 3),
+                    2.0 ** -9 * np.repeat(s, 128, axis=-1)[..., :300, None])
+    assert np.all(np.abs(xh - x) <= 0.5 * step + 1e-45)
