@@ -152,6 +152,32 @@ class Fp8:
                 "mask": w.mask, "qk": "e4m3fn, fp32 scale per 128 rows", "v": "bf16", "seed": self.seed}
 
 
+class Fp8Full(Fp8):
+    """attn_fwd_fp8_full: V in fp8 as well (power-of-two block scales)."""
+
+    def __init__(self, key, seed):
+        import torch
+        from tiled_attention_amd import _lib as A
+        from tiled_attention_amd import workloads as wl
+        super().__init__(key, seed)
+        w = self.w
+        v = wl.dense_inputs(w.B, w.H, w.N, w.d, seed=seed, outlier_p=w.outlier_p, outlier_scale=w.outlier_scale)[2]
+        self.v8 = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+        self.sv = torch.empty_like(self.sq)
+        A.attn_quant_fp8_block_pow2(torch.from_numpy(v).cuda(), self.v8, self.sv)
+        torch.cuda.synchronize()
+
+        def step():
+            A.attn_fwd_fp8_full(self.q8, self.sq, self.k8, self.sk, self.v8, self.sv, self.o, w.scale, w.mask)
+        self.step = step
+
+    def describe(self):
+        d = super().describe()
+        d["v"] = "e4m3fn, power-of-two scale per 128 rows"
+        d["p"] = "e4m3fn"
+        return d
+
+
 class Paged:
     def __init__(self, key, seed):
         import torch
@@ -344,7 +370,8 @@ def main():
     def make(key):
         seed = args.seed if args.seed is not None else wl.default_seed(key)
         w = wl.WORKLOADS[key]
-        return {"paged": Paged, "fp8": Fp8, "paged_prefill": PagedPrefill, "paged_cross": PagedCross}.get(
+        return {"paged": Paged, "fp8": Fp8, "fp8_full": Fp8Full, "paged_prefill": PagedPrefill,
+                "paged_cross": PagedCross}.get(
             w.kind, Dense)(key, seed)
 
     if args.copy_calibration_mib > 0:
@@ -394,14 +421,14 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if not isinstance(wk, Fp8) else "fp8e4m3+bf16",
+        "vs_baseline": None, "dtype": "fp8e4m3" if isinstance(wk, Fp8Full) else "fp8e4m3+bf16" if isinstance(wk, Fp8) else "bf16",
         "data": "synthetic", "config": wk.describe(), "roofline": roof,
     }
 
     if not args.only_main:
         others = {}
         for key, reps in ((1, 200), (3, 20), (4, 20), (5, 20), (6, 20), (7, 20), (8, 10), (9, 20), (10, 20),
-                          (11, 20), (12, 20)):
+                          (11, 20), (12, 20), (13, 20)):
             log(f"bench: workload {key}")
             o = make(key)
             avg, med, mn = event_time_ms(o.step, reps)
@@ -414,7 +441,9 @@ def main():
             else:
                 tf = o.flops / (avg * 1e-3) / 1e12
                 entry.update({"value": round(tf, 2), "unit": "TFLOP/s", "algorithmic_flops": o.flops})
-                if isinstance(o, Fp8):
+                if isinstance(o, Fp8Full):
+                    entry.update({"frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)})
+                elif isinstance(o, Fp8):
                     half = o.flops / 2
                     blended_s = half / (PEAK_FP8_TFLOPS * 1e12) + half / (PEAK_BF16_TFLOPS * 1e12)
                     entry.update({"frac_of_blended_peak": round(blended_s / (avg * 1e-3), 4),

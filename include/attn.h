@@ -133,6 +133,27 @@ attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale,
                          float* lse, void* stream);
 
 /*
+ * attn_fwd_fp8_full -- prefill with Q, K and V all fp8: S as in attn_fwd_fp8,
+ * and P V on the fp8 matrix cores with P rounded to E4M3 (P <= 448 is kept by
+ * the softmax reference). This extends the block quantisation of
+ * "FlashAttention-3 ...", "FP8 Block Quantization", which the page applies
+ * to Q and K, to the second product.
+ *   v8      : [B, H, N, d] E4M3FN codes.
+ *   v_scale : [B, H, ceil(N/qk_block)] fp32, each a power of two in
+ *             [2^-127, 2^127] (attn_quant_fp8_block_pow2 writes such scales);
+ *             the matrix core applies it as an exponent, so a scale that is
+ *             not a power of two acts as the power of two at or below it.
+ *   other arguments and the output as attn_fwd_fp8 (o bf16).
+ */
+attn_status attn_fwd_fp8_full(const uint8_t* q8, const float* q_scale,
+                              const uint8_t* k8, const float* k_scale,
+                              const uint8_t* v8, const float* v_scale, void* o,
+                              int B, int H, int N, int d, int qk_block,
+                              float scale, attn_mask mask, int window,
+                              const int32_t* doc_offsets, int num_docs,
+                              float* lse, void* stream);
+
+/*
  * attn_quant_fp8_block -- per-block E4M3FN quantisation of x [B, H, N, d] fp32
  * ("FlashAttention-3 ...", "FP8 Block Quantization"): for every 128-row
  * block (the last may be ragged) s = fp32(absmax) / 448 (IEEE fp32 division;
@@ -143,6 +164,16 @@ attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale,
  */
 attn_status attn_quant_fp8_block(const float* x, uint8_t* codes, float* scales,
                                  int B, int H, int N, int d, int block, void* stream);
+
+/*
+ * attn_quant_fp8_block_pow2 -- as attn_quant_fp8_block, with each block's
+ * scale rounded up to a power of two: s = 2^k, the smallest with
+ * absmax / s <= 448 (k >= -127; s = 1 for an all-zero block), decided on the
+ * exact binary mantissa of absmax. code = e4m3(x / s) (an exact division).
+ * For V of attn_fwd_fp8_full.
+ */
+attn_status attn_quant_fp8_block_pow2(const float* x, uint8_t* codes, float* scales,
+                                      int B, int H, int N, int d, int block, void* stream);
 
 /*
  * Paged KV cache ("Optimizing Triton kernels ...", Pattern C).

@@ -20,6 +20,22 @@ FP8_REL_RMSE = 5e-2
 # need, -log(1 - 2^-9) = 1.955e-3 plus fp32 slack, which also covers the
 # kernels that sum the rounded weights.
 LSE_TOL_MFMA = 2.5e-3
+# The fp8 matrix cores multiply E4M3 codes exactly but accumulate the raw code
+# products (up to 448^2 each) in fp32 before the block scales apply, so a score
+# carries the fp32 rounding of sums far larger than itself. With the outlier
+# workloads (LSE near 130) this measured 3.3e-4 of |LSE|; the fp8 paths' LSE is
+# held to 2e-3 of max(1, |LSE|).
+LSE_REL_TOL_FP8 = 2e-3
+
+
+def check_lse_fp8(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    live = np.isfinite(ref)
+    assert np.all(got[~live] == -np.inf)
+    err = np.abs(got[live] - ref[live]) / np.maximum(1.0, np.abs(ref[live]))
+    assert err.max() <= LSE_REL_TOL_FP8, f"fp8 LSE relative error {err.max():.3g}"
+    return float(err.max())
 
 
 def say(*a):

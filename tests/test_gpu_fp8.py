@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from parity import FP8_REL_RMSE, cuda, rel_rmse, sample_rows, say, to_np
+from parity import FP8_REL_RMSE, check_lse_fp8, cuda, rel_rmse, sample_rows, say, to_np
 from tiled_attention_amd import _lib as A
 from tiled_attention_amd import workloads as wl
 
@@ -48,8 +48,9 @@ def _fp8_case(B, H, N, d, mask, window, seed, rows=None, heads=None):
     q8, sq = _quant_gpu(q)
     k8, sk = _quant_gpu(k)
     o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(d)
-    A.attn_fwd_fp8(q8, sq, k8, sk, cuda(vb), o, scale, mask, window)
+    A.attn_fwd_fp8(q8, sq, k8, sk, cuda(vb), o, scale, mask, window, lse=lse)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all()
     qh = oracle.dequantize_blocks(q8.cpu().numpy(), sq.cpu().numpy())
@@ -59,7 +60,8 @@ def _fp8_case(B, H, N, d, mask, window, seed, rows=None, heads=None):
     got, ref_hat, ref_orig = [], [], []
     for b, h in heads:
         r = rows if rows is not None else None
-        oh, _ = oracle.attention(qh[b, h], kh[b, h], wl.bf16_to_f64(vb[b, h]), scale, mask, win, rows=r)
+        oh, lh = oracle.attention(qh[b, h], kh[b, h], wl.bf16_to_f64(vb[b, h]), scale, mask, win, rows=r)
+        check_lse_fp8(to_np(lse[b, h]) if r is None else to_np(lse[b, h])[r], lh)
         oo, _ = oracle.attention(q[b, h].astype(np.float64), k[b, h].astype(np.float64),
                                  wl.bf16_to_f64(vb[b, h]), scale, mask, win, rows=r)
         g = to_np(o[b, h])

@@ -1,0 +1,96 @@
+"""GPU parity of the all-fp8 path: the power-of-two block quantiser (bit-exact
+codes and scales against the oracle) and attn_fwd_fp8_full (relative RMSE
+against the oracle run on the dequantised Q, K and V, as for the fp8 Q/K
+path). The bar is the fp8 one, 5e-2. P is rounded to E4M3 for the second
+product: 3 mantissa bits, so a relative error of at most 2^-4 per weight
+(2^-4 / sqrt(3) = 3.6% RMS), averaged over the effective number of keys of a
+row; the tests also hold the kernel to 2e-2, which that rounding allows for
+rows of two or more effective keys."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import FP8_REL_RMSE, check_lse_fp8, cuda, rel_rmse, sample_rows, say, to_np
+from tiled_attention_amd import _lib as A
+from tiled_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+P_ROUNDING_RMSE = 2e-2
+
+
+def _quant(x, pow2):
+    xg = cuda(torch.from_numpy(x))
+    B, H, N, d = x.shape
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((B, H, -(-N // 128)), dtype=torch.float32, device="cuda")
+    (A.attn_quant_fp8_block_pow2 if pow2 else A.attn_quant_fp8_block)(xg, codes, scales)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 300, 64), (2, 1, 128, 128), (1, 1, 1, 128), (1, 3, 1000, 128)])
+def test_pow2_quantiser_bit_exact(shape):
+    x = wl.dense_inputs(*shape, seed=sum(shape) + 1, outlier_p=0.01, outlier_scale=20.0)[2]
+    if shape[2] >= 256:
+        x[0, 0, 128:256] = 0.0                       # an all-zero block
+        x[0, -1, 0:128] *= np.float32(2.0 ** -100)   # a tiny block
+        x[0, -1, 128:256] = np.float32(448.0 * 2 ** -7)   # absmax / 448 exactly a power of two
+    codes, scales = _quant(x, True)
+    rc, rs = oracle.quantize_blocks(x, pow2=True)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def _full(B, H, N, d, mask, window, seed, offs=None):
+    q, k, v = wl.dense_inputs(B, H, N, d, seed=seed, outlier_p=0.01, outlier_scale=20.0)
+    q8, sq = _quant(q, False)
+    k8, sk = _quant(k, False)
+    v8, sv = _quant(v, True)
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    doc = None if offs is None else torch.from_numpy(np.asarray(offs, dtype=np.int32)).cuda()
+    A.attn_fwd_fp8_full(q8, sq, k8, sk, v8, sv, o, 1.0 / math.sqrt(d), mask, window, doc_offsets=doc, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    deq = [oracle.dequantize_blocks(c.cpu().numpy(), s_.cpu().numpy()) for c, s_ in ((q8, sq), (k8, sk), (v8, sv))]
+    return o, lse, deq, (q, k, v)
+
+
+@pytest.mark.parametrize("case", [(1, 2, 300, 64, "causal", 0), (1, 2, 257, 128, "causal", 0),
+                                  (2, 1, 640, 128, "none", 0), (1, 2, 1000, 128, "sliding", 300),
+                                  (1, 1, 1, 128, "causal", 0), (1, 2, 513, 64, "none", 0),
+                                  (1, 2, 900, 128, "document", 0)], ids=lambda c: "-".join(map(str, c)))
+def test_fp8_full_small(case):
+    B, H, N, d, mask, window = case
+    say(f"fp8 full {case}")
+    offs = wl.document_offsets(N, 5, 300, 3) if mask == "document" else None
+    o, lse, (qh, kh, vh), _ = _full(B, H, N, d, mask, window, seed=50 + N + d, offs=offs)
+    win = window if mask == "sliding" else None
+    ref, ref_lse = oracle.attention(qh, kh, vh, 1.0 / math.sqrt(d), mask, win, doc_offsets=offs)
+    rr = rel_rmse(to_np(o), ref)
+    say(f"  rel RMSE vs dequantised oracle {rr:.3g}")
+    assert rr <= min(FP8_REL_RMSE, P_ROUNDING_RMSE)
+    check_lse_fp8(to_np(lse), ref_lse)
+
+
+def test_fp8_full_workload_sampled():
+    w = wl.WORKLOADS[13]
+    seed = wl.default_seed(13)
+    say(f"{w.name}: generating and quantising (seed {seed})")
+    o, _, (qh, kh, vh), (q, k, v) = _full(w.B, w.H, w.N, w.d, w.mask, 0, seed)
+    got, ref, orig = [], [], []
+    for h in (0, 7, 15):
+        rows = sample_rows(w.N, seed + h)
+        r, _ = oracle.attention(qh[0, h], kh[0, h], vh[0, h], w.scale, w.mask, rows=rows)
+        r0, _ = oracle.attention(q[0, h], k[0, h], v[0, h], w.scale, w.mask, rows=rows)
+        got.append(to_np(o[0, h][rows]))
+        ref.append(r)
+        orig.append(r0)
+    rr = rel_rmse(np.concatenate(got), np.concatenate(ref))
+    rr0 = rel_rmse(np.concatenate(got), np.concatenate(orig))
+    say(f"{w.name}: rel RMSE {rr:.3g} vs dequantised oracle, {rr0:.3g} vs the fp32-input oracle (reported)")
+    assert rr <= min(FP8_REL_RMSE, P_ROUNDING_RMSE)

@@ -8,7 +8,9 @@ same entry-point names, the build script and the seeded workload generators.
 from ._lib import (  # noqa: F401
     attn_fwd,
     attn_fwd_fp8,
+    attn_fwd_fp8_full,
     attn_quant_fp8_block,
+    attn_quant_fp8_block_pow2,
     attn_decode_paged_workspace_size,
     attn_decode_paged,
     attn_gather_paged,

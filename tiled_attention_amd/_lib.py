@@ -26,7 +26,10 @@ _PROTOS = {
                           _c_int, _c_int, _p, _c_int, _p, _p]),
     "attn_fwd_fp8": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                               _c_int, _c_int, _p, _c_int, _p, _p]),
+    "attn_fwd_fp8_full": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_float, _c_int, _c_int, _p, _c_int, _p, _p]),
     "attn_quant_fp8_block": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),
+    "attn_quant_fp8_block_pow2": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),
     "attn_decode_paged_workspace_size": (_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_decode_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_float, _p, _p, _size, _p]),
@@ -144,6 +147,28 @@ def attn_fwd_fp8(q8, q_scale, k8, k_scale, v, o, scale, mask="none", window=0, d
                                B, H, N, d, int(qk_block), float(scale), MASKS[mask], int(window), dp, nd,
                                _ptr(lse), _stream(stream)))
     return o
+
+
+def attn_fwd_fp8_full(q8, q_scale, k8, k_scale, v8, v_scale, o, scale, mask="none", window=0, doc_offsets=None,
+                      qk_block=128, lse=None, stream=None):
+    """Q, K and V all fp8 (uint8 E4M3FN codes + fp32 block scales; V's scales powers of two), bf16 O."""
+    _dev(q8, q_scale, k8, k_scale, v8, v_scale, o, lse)
+    _require(q8.dim() == 4 and q8.shape == k8.shape == v8.shape == o.shape, "shapes must be [B, H, N, d]")
+    B, H, N, d = q8.shape
+    dp, nd = _docs(mask, doc_offsets)
+    _check(load().attn_fwd_fp8_full(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale),
+                                    _ptr(o), B, H, N, d, int(qk_block), float(scale), MASKS[mask], int(window), dp,
+                                    nd, _ptr(lse), _stream(stream)))
+    return o
+
+
+def attn_quant_fp8_block_pow2(x, codes, scales, block=128, stream=None):
+    """As attn_quant_fp8_block with power-of-two block scales (for V of attn_fwd_fp8_full)."""
+    _dev(x, codes, scales)
+    B, H, N, d = x.shape
+    _check(load().attn_quant_fp8_block_pow2(_ptr(x), _ptr(codes), _ptr(scales), B, H, N, d, int(block),
+                                            _stream(stream)))
+    return codes, scales
 
 
 def attn_quant_fp8_block(x, codes, scales, block=128, stream=None):

@@ -88,13 +88,14 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, int B
   return launched(attn::launch_fwd(a, (hipStream_t)stream));
 }
 
-attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
-                         const void* v, void* o, int B, int H, int N, int d, int qk_block, float scale,
-                         attn_mask mask, int window, const int32_t* doc_offsets, int num_docs, float* lse,
-                         void* stream) {
-  if (!q8 || !q_scale || !k8 || !k_scale || !v || !o) return ATTN_ERR_INVALID_ARG;
+static attn_status fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                           const void* v, const float* v_scale, bool v8, void* o, int B, int H, int N, int d,
+                           int qk_block, float scale, attn_mask mask, int window, const int32_t* doc_offsets,
+                           int num_docs, float* lse, void* stream) {
+  if (!q8 || !q_scale || !k8 || !k_scale || !v || !o || (v8 && !v_scale)) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
-  if (((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+    return ATTN_ERR_INVALID_ARG;
   if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
   if (!valid_mask(mask, window, doc_offsets, num_docs)) return ATTN_ERR_INVALID_ARG;
   if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
@@ -110,6 +111,7 @@ attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t*
   a.lse = lse;
   a.q_scale = q_scale;
   a.k_scale = k_scale;
+  a.v_scale = v8 ? v_scale : nullptr;
   a.BH = B * H;
   a.N = N;
   a.d = d;
@@ -118,18 +120,45 @@ attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t*
   a.in_f32 = false;
   a.out_f32 = false;
   a.fp8 = true;
+  a.v8 = v8;
   return launched(attn::launch_fwd(a, (hipStream_t)stream));
 }
 
-attn_status attn_quant_fp8_block(const float* x, uint8_t* codes, float* scales, int B, int H, int N, int d,
-                                 int block, void* stream) {
+attn_status attn_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                         const void* v, void* o, int B, int H, int N, int d, int qk_block, float scale,
+                         attn_mask mask, int window, const int32_t* doc_offsets, int num_docs, float* lse,
+                         void* stream) {
+  return fwd_fp8(q8, q_scale, k8, k_scale, v, nullptr, false, o, B, H, N, d, qk_block, scale, mask, window,
+                 doc_offsets, num_docs, lse, stream);
+}
+
+attn_status attn_fwd_fp8_full(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                              const uint8_t* v8, const float* v_scale, void* o, int B, int H, int N, int d,
+                              int qk_block, float scale, attn_mask mask, int window, const int32_t* doc_offsets,
+                              int num_docs, float* lse, void* stream) {
+  return fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, true, o, B, H, N, d, qk_block, scale, mask, window,
+                 doc_offsets, num_docs, lse, stream);
+}
+
+static attn_status quant(const float* x, uint8_t* codes, float* scales, int B, int H, int N, int d, int block,
+                         bool pow2, void* stream) {
   if (!x || !codes || !scales) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 3u)) return ATTN_ERR_INVALID_ARG;
   if (block < 1) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_dims(B, H, N, d);
   if (st != ATTN_OK) return st;
   if (block != 128) return ATTN_ERR_UNSUPPORTED;
-  return launched(attn::launch_quant_fp8(x, codes, scales, B * H, N, d, (hipStream_t)stream));
+  return launched(attn::launch_quant_fp8(x, codes, scales, B * H, N, d, pow2, (hipStream_t)stream));
+}
+
+attn_status attn_quant_fp8_block(const float* x, uint8_t* codes, float* scales, int B, int H, int N, int d,
+                                 int block, void* stream) {
+  return quant(x, codes, scales, B, H, N, d, block, false, stream);
+}
+
+attn_status attn_quant_fp8_block_pow2(const float* x, uint8_t* codes, float* scales, int B, int H, int N, int d,
+                                      int block, void* stream) {
+  return quant(x, codes, scales, B, H, N, d, block, true, stream);
 }
 
 size_t attn_decode_paged_workspace_size(int S, int H, int d, int max_pages, int page_size) {

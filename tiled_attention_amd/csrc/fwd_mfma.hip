@@ -76,11 +76,21 @@ constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 (gfx9 raw 
 // A lane's partial sum of one tile's P above this moves the reference. P <=
 // 2^24 leaves acc and l far from the fp32 range for any sequence length.
 constexpr float kSumLimit = 16777216.f;
+// With P in fp8 (E4M3, largest value 448) the same bound is 448: it caps every P.
+constexpr float kSumLimitFp8 = 448.f;
+// With P in fp8, P is formed scaled by 2^3 (and the matrix core scales the
+// product back by 2^-3): E4M3 is normal only from 2^-6, and over long rows most
+// weights are small. 2^3 is the largest factor that keeps 32 weights of at
+// most 1 (a lane's share of a tile right after the reference moved) under the
+// 448 bound, so it adds no reference moves.
+constexpr int kPShiftFp8 = 3;
 
-template <int D, bool FP8>
+// V8: V is fp8 too (codes with power-of-two block scales) and P V runs on the
+// fp8 matrix cores.
+template <int D, bool FP8, bool V8 = false>
 struct Cfg {
   static constexpr int KROW = FP8 ? D : 2 * D;  // bytes per K row
-  static constexpr int VROW = 2 * D;            // bytes per V row
+  static constexpr int VROW = V8 ? D : 2 * D;   // bytes per V row
   static constexpr int K_SLOT = BN * KROW;
   static constexpr int V_SLOT = BN * VROW;
   static constexpr int KLD = K_SLOT / (16 * NT);  // DMA loads per thread per K tile
@@ -111,6 +121,23 @@ __device__ __forceinline__ int swz_v(int row) {
   static_assert(ROWB == 128 || ROWB == 256, "row size");
   return ROWB == 128 ? ((row >> 1) & 1) << 2 : (row & 3) << 2;
 }
+//  K with fp8 V (rows read in the order 0-3, 32-35, 4-7, 36-39, ... by 16
+//    lanes): row bit 5 joins the swizzle so rows 32 apart differ too; rows 16
+//    apart (the second key block) keep the same swizzle.
+template <int ROWB>
+__device__ __forceinline__ int swz_k8(int row) {
+  static_assert(ROWB == 64 || ROWB == 128, "row size");
+  return ROWB == 64 ? ((row >> 2) & 1) | (((row >> 5) & 1) << 1) : ((row >> 1) & 3) | (((row >> 5) & 1) << 2);
+}
+//  fp8 V (8-bit transposed reads: 8 consecutive rows x 16 bytes per 16 lanes):
+//    the even rows (and the odd rows) of an 8-row run land on distinct chunks.
+//    Only row bits 1-2 (64-byte rows: bit 2) are used, so rows 8 apart share
+//    the swizzle.
+template <int ROWB>
+__device__ __forceinline__ int swz_v8(int row) {
+  static_assert(ROWB == 64 || ROWB == 128, "row size");
+  return ROWB == 64 ? (row >> 2) & 1 : (row >> 1) & 3;
+}
 
 struct Params {
   const void* q;
@@ -120,6 +147,7 @@ struct Params {
   float* lse;
   const float* q_scale;
   const float* k_scale;
+  const float* v_scale;
   const int32_t* doc;
   int N, mask, window, nd, n_qtiles, units_per_bh, units, pair, nsb;
   // paged K/V: k, v are [pool pages, H, 64, d] pools; (sequence s, query
@@ -198,15 +226,25 @@ struct TileStream {
   }
 };
 
-template <int D, bool FP8, bool OUT_F32, bool PG>
+template <int D, bool FP8, bool OUT_F32, bool PG, bool V8>
 struct QTile {
   static_assert(!(PG && FP8), "paged K/V is bf16");
-  using C = Cfg<D, FP8>;
+  static_assert(!V8 || FP8, "fp8 V comes with fp8 Q and K");
+  using C = Cfg<D, FP8, V8>;
   static constexpr int KROW = C::KROW, VROW = C::VROW, QK_STEPS = C::QK_STEPS, DE = C::DE;
   static constexpr int KLD = C::KLD, VLD = C::VLD, L = KLD + VLD, NS = C::NS, U = C::U;
   // per step: LDS operand reads and MFMAs
-  static constexpr int kStepReads = 2 * QK_STEPS * (FP8 ? 2 : 1) + 8 * DE;
-  static constexpr int kStepMfma = 2 * QK_STEPS + 4 * DE;
+  static constexpr int kStepReads = 2 * QK_STEPS * (FP8 ? 2 : 1) + (V8 ? 4 : 8) * DE;
+  static constexpr int kStepMfma = 2 * QK_STEPS + (V8 ? 1 : 4) * DE;
+  static constexpr float kLimit = V8 ? kSumLimitFp8 : kSumLimit;
+  // S^T rows of key block 1 sit this many K rows after block 0's
+  static constexpr int kBlock1Rows = V8 ? 16 : 32;
+  static __device__ __forceinline__ int kswz(int row) {
+    if constexpr (V8)
+      return swz_k8<KROW>(row);
+    else
+      return swz_k<KROW>(row);
+  }
   typedef typename std::conditional<FP8, i32x8, bf16x8>::type QFrag;
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
@@ -233,9 +271,11 @@ struct QTile {
   float limit;              // largest tile sum of P that keeps m_ref (-1 while it is -inf)
   float c_next;             // fp8: score scale of the next tile, loaded a step ahead
   float l_run;              // this lane's share of the row sum
+  int vq0, vq1;             // fp8 V: scale exponents (E8M0) of tiles i and i+1 at step i+1
   f32x16 oacc[DE];
   f32x16 S[2][2];           // S^T of two tiles: [buffer][key block]
   bf16x8 P[2][4];           // P of two tiles: [buffer][k-step]
+  i32x8 P8[2];              // fp8 V: P of two tiles as fp8 bytes, byte k = key 32 hl + k
 
   __device__ __forceinline__ QTile(const Params& p_, unsigned char* smem_, int bh_, int qt) : p(p_), smem(smem_) {
     const int tid = threadIdx.x;
@@ -304,32 +344,56 @@ struct QTile {
     for (int u = 0; u < KLD; ++u) {
       const int off = (u * NW + wave) * 1024 + lane * 16;
       const int row = off / KROW, ch = (off % KROW) / 16;
-      kdma[u] = row * KROW + 16 * (ch ^ swz_k<KROW>(row));
+      kdma[u] = row * KROW + 16 * (ch ^ kswz(row));
     }
 #pragma unroll
     for (int u = 0; u < VLD; ++u) {
       const int off = (u * NW + wave) * 1024 + lane * 16;
       const int row = off / VROW, ch = (off % VROW) / 16;
-      vdma[u] = row * VROW + 16 * (ch ^ swz_v<VROW>(row));
+      if constexpr (V8)
+        vdma[u] = row * VROW + 16 * (ch ^ swz_v8<VROW>(row));
+      else
+        vdma[u] = row * VROW + 16 * (ch ^ swz_v<VROW>(row));
     }
-    // K read of k-step t: row l32 (block b adds 32 rows, same swizzle), chunk of half hl
+    // K read of k-step t: lane l32 supplies S^T row l32 of block 0 (block 1:
+    // kBlock1Rows further, same swizzle), chunk of half hl. With fp8 V the
+    // rows are permuted so that lane (row l32, half hl) ends up holding keys
+    // 32 hl .. 32 hl + 31 of the tile: row 8j + 4h + t reads key 32h + 4j + t.
+    const int krow = V8 ? 32 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3) : l32;
     constexpr int KCH_STEP = FP8 ? 4 : 2;  // 16-byte chunks per k-step
 #pragma unroll
     for (int t = 0; t < QK_STEPS; ++t) {
       if constexpr (FP8) {
         const int c0 = KCH_STEP * t + 2 * hl;
-        kread[2 * t] = l32 * KROW + 16 * (c0 ^ swz_k<KROW>(l32));
-        kread[2 * t + 1] = l32 * KROW + 16 * ((c0 + 1) ^ swz_k<KROW>(l32));
+        kread[2 * t] = krow * KROW + 16 * (c0 ^ kswz(krow));
+        kread[2 * t + 1] = krow * KROW + 16 * ((c0 + 1) ^ kswz(krow));
       } else {
-        kread[t] = l32 * KROW + 16 * ((KCH_STEP * t + hl) ^ swz_k<KROW>(l32));
+        kread[t] = krow * KROW + 16 * ((KCH_STEP * t + hl) ^ kswz(krow));
       }
     }
-    // transposed V read: 16-lane group g, row rr of 4, 8-byte column piece cc
-    const int g = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
-    const int sv = swz_v<VROW>(4 * hl + rr);   // same for rows +16q and +8
+    if constexpr (V8) {
+      // 8-bit transposed V reads: in each 16-lane group, output lane j takes
+      // byte j % 8 of the 8 bytes that lanes 2m + j / 8 (m = 0..7) point at.
+      // Lane l points at key 32 hl + 8 i + (l % 16) / 2 (read i = 0..3) and at
+      // dims 32 e + 16 ((l >> 4) & 1) + 8 (l & 1) .. + 7, so lane l receives
+      // dim 32 e + l % 32 of keys 32 hl + 8 i .. + 7: the A operand of the fp8
+      // MFMA (row = dim, k = key - 32 hl). Row bases for even and odd e: the
+      // swizzle flips chunk bit 1 (dim block parity) and bit 0 (half).
+      const int row0 = 32 * hl + ((lane & 15) >> 1);
+      const int g1 = (lane >> 4) & 1;
+      const int sw = swz_v8<VROW>(row0);
+      const int base = row0 * VROW + 16 * (g1 ^ (sw & 1)) + 8 * (lane & 1);
+      const int s1 = VROW == 128 ? (sw >> 1) & 1 : 0;
+      vread[0] = base + 32 * s1;
+      vread[1] = base - 32 * s1;
+    } else {
+      // transposed V read: 16-lane group g, row rr of 4, 8-byte column piece cc
+      const int g = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
+      const int sv = swz_v<VROW>(4 * hl + rr);   // same for rows +16q and +8
 #pragma unroll
-    for (int e = 0; e < DE; ++e)
-      vread[e] = (4 * hl + rr) * VROW + 16 * ((4 * e + 2 * (g & 1) + (cc >> 1)) ^ sv) + 8 * (cc & 1);
+      for (int e = 0; e < DE; ++e)
+        vread[e] = (4 * hl + rr) * VROW + 16 * ((4 * e + 2 * (g & 1) + (cc >> 1)) ^ sv) + 8 * (cc & 1);
+    }
 
     const uint32_t lds0 = lds_addr(smem);
     lds_k = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
@@ -348,6 +412,8 @@ struct QTile {
     m_use = 0.f;
     limit = -1.f;
     c_next = tile_scale(0);
+    vq0 = 127;                // the tile before the first: P is 0 there
+    vq1 = v_exponent(0);
     l_run = 0.f;
   }
 
@@ -428,15 +494,15 @@ struct QTile {
       if constexpr (FP8) {
         const i32x4 a0l = *(const i32x4*)(ksl + kread[2 * t]);
         const i32x4 a0h = *(const i32x4*)(ksl + kread[2 * t + 1]);
-        const i32x4 a1l = *(const i32x4*)(ksl + kread[2 * t] + 32 * KROW);
-        const i32x4 a1h = *(const i32x4*)(ksl + kread[2 * t + 1] + 32 * KROW);
+        const i32x4 a1l = *(const i32x4*)(ksl + kread[2 * t] + kBlock1Rows * KROW);
+        const i32x4 a1h = *(const i32x4*)(ksl + kread[2 * t + 1] + kBlock1Rows * KROW);
         const i32x8 a0 = {a0l[0], a0l[1], a0l[2], a0l[3], a0h[0], a0h[1], a0h[2], a0h[3]};
         const i32x8 a1 = {a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]};
         s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qf[t], s0, 0, 0, 0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qf[t], s1, 0, 0, 0, 0, 0, 0);
       } else {
         const bf16x8 a0 = *(const bf16x8*)(ksl + kread[t]);
-        const bf16x8 a1 = *(const bf16x8*)(ksl + kread[t] + 32 * KROW);
+        const bf16x8 a1 = *(const bf16x8*)(ksl + kread[t] + kBlock1Rows * KROW);
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[t], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[t], s1, 0, 0, 0);
       }
@@ -445,10 +511,26 @@ struct QTile {
     S[B][1] = s1;
   }
 
-  // O^T += V^T P^T for the V tile in slot SLOT and the P in P[B]
+  // O^T += V^T P^T for the V tile in slot SLOT and the P in P[B] (fp8 V: the
+  // tile's scale exponent vexp is applied by the matrix core)
   template <int SLOT, int B>
-  __device__ __forceinline__ void pv() {
+  __device__ __forceinline__ void pv(int vexp) {
     const unsigned char* vsl = smem + NS * C::K_SLOT + SLOT * C::V_SLOT;
+    if constexpr (V8) {
+      typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+#pragma unroll
+      for (int e = 0; e < DE; ++e) {
+        const unsigned char* vp = vsl + vread[e & 1] + 32 * e;
+        i32x2 r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          r[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(vp + 8 * i * VROW));
+        const i32x8 a = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+        oacc[e] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P8[B], oacc[e], 0, 0, 0, vexp, 0,
+                                                                 127 - kPShiftFp8);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -463,6 +545,16 @@ struct QTile {
     }
   }
 
+  // reference the exponentials subtract: fp8 P is formed 2^kPShiftFp8 times larger
+  __device__ __forceinline__ float m_exp() const { return V8 ? m_use - (float)kPShiftFp8 : m_use; }
+
+  // fp8 V: E8M0 exponent (biased by 127) of local tile i's power-of-two V scale
+  __device__ __forceinline__ int v_exponent(int i) const {
+    if constexpr (!V8) return 127;
+    const float s = p.v_scale[bh * p.nsb + ((t_lo + max(min(i, NK - 1), 0)) * BN) / 128];
+    return (int)((__float_as_uint(s) >> 23) & 0xFFu);
+  }
+
   // log2-domain score scale of local tile i (fp8: times the two blocks' scales)
   __device__ __forceinline__ float tile_scale(int i) const {
     float c = p.scale_log2;
@@ -473,16 +565,16 @@ struct QTile {
   // S[B] of local tile i: -inf where the key is not visible to the lane's row
   template <int B>
   __device__ __forceinline__ void mask(int i) {
-    // key of S[B][b][r] is n0 + 32b + 8(r/4) + 4hl + r%4
+    // key of S[B][b][r] is n0 + 32b + 8(r/4) + 4hl + r%4 (fp8 V: n0 + 32hl + 16b + r)
     // visible offsets kc: lo < kc <= hi (the interval ends before N)
-    const int n0 = (t_lo + i) * BN + 4 * hl;
+    const int n0 = (t_lo + i) * BN + (V8 ? 32 : 4) * hl;
     const int hi = khi - n0;
     const int lo = klo_m1 - n0;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kc = 32 * b + 8 * (r >> 2) + (r & 3);
+        const int kc = V8 ? 16 * b + r : 32 * b + 8 * (r >> 2) + (r & 3);
         const bool vis = (kc <= hi) & (kc > lo);
         S[B][b][r] = vis ? S[B][b][r] : -INFINITY;
       }
@@ -500,8 +592,16 @@ struct QTile {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         e[8 * q + j] = fast_exp2(__builtin_fmaf(S[B][q >> 1][8 * (q & 1) + j], c, -m_use));
-        P[B][q][j] = (__bf16)e[8 * q + j];
+        if constexpr (!V8) P[B][q][j] = (__bf16)e[8 * q + j];
       }
+    if constexpr (V8) {
+      // byte k of the B operand is e[k] (key 32 hl + k), rounded to E4M3
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
+        P8[B][w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], d, true);
+      }
+    }
 #pragma unroll
     for (int w = 16; w >= 1; w >>= 1)
 #pragma unroll
@@ -523,8 +623,8 @@ struct QTile {
     const float alpha = m_new == m_ref ? 1.f : fast_exp2(m_ref - m_new);
     m_ref = m_new;
     m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    limit = m_ref == -INFINITY ? -1.f : kSumLimit;
-    psum = exponentials<B>(c, m_use);
+    limit = m_ref == -INFINITY ? -1.f : kLimit;
+    psum = exponentials<B>(c, m_exp());
     l_run *= alpha;
 #pragma unroll
     for (int e = 0; e < DE; ++e)
@@ -541,11 +641,18 @@ struct QTile {
     // {K_{i+1}, V_{i-1}} landed; every wave is done with K_i and V_{i-2}
     sync_tiles<(NS - 2) * L>();
     float c = p.scale_log2;
+    int vpv = 127;
     if constexpr (FP8) {
-      // the scale loaded a step ago: waited for here, before this step's LDS reads
+      // the scales loaded a step ago: waited for here, before this step's LDS reads
       c = c_next;
       asm volatile("" : "+v"(c));
       c_next = tile_scale(i + 1);
+      if constexpr (V8) {
+        asm volatile("" : "+v"(vq1));
+        vpv = vq0;            // tile i - 1, whose P V runs now
+        vq0 = vq1;            // tile i
+        vq1 = v_exponent(i + 1);
+      }
     }
     // refill the slots freed at this step's sync_tiles. A ring of 2 or 3
     // slots is refilled at once, so the tiles have a whole step to land
@@ -557,8 +664,8 @@ struct QTile {
     // unconditional, so the block has no branch: for i + 1 == NK the slot
     // holds a tile past the band whose scores are never used
     qk<(PH + 1) % NS, BO>();
-    pv<(PH + NS - 1) % NS, BO>();
-    float psum = exponentials<B>(c, m_use);
+    pv<(PH + NS - 1) % NS, BO>(vpv);
+    float psum = exponentials<B>(c, m_exp());
     // issue order: every LDS operand read of the step first, then each MFMA
     // followed by a run of the softmax VALU work
     __builtin_amdgcn_sched_group_barrier(0x100, kStepReads, 0);
@@ -570,7 +677,8 @@ struct QTile {
     // a lane without a reference yet, or a tile sum past the limit, moves it
     // (before P V of the tile, which the next step issues)
     if (__builtin_expect(__any(!(psum <= limit)), 0)) rebase<B>(c, psum);
-    l_run += psum;
+    // the sum of P itself (fp8 P: the sum of the scaled values times 2^-3)
+    l_run += V8 ? psum * (1.f / (1 << kPShiftFp8)) : psum;
     if constexpr (!kEarlyRefill) refill<PH>();
   }
 
@@ -590,7 +698,7 @@ struct QTile {
   template <int PH>
   __device__ __forceinline__ void drain() {
     sync_tiles<(NS - 2) * L>();
-    pv<PH % NS, PH & 1>();
+    pv<PH % NS, PH & 1>(vq0);
   }
 
   template <int... PHS>
@@ -640,6 +748,7 @@ struct QTile {
     sync_tiles<0>();
 #pragma unroll
     for (int q = 0; q < 4; ++q) P[1][q] = (bf16x8){};
+    P8[1] = (i32x8){};
     if (NK > 0) qk<0, 0>();
 
     int i = 0;
@@ -744,9 +853,9 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
   }
 }
 
-template <int D, bool FP8, bool OUT_F32, bool PG>
+template <int D, bool FP8, bool OUT_F32, bool PG, bool V8>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8>::LDS + (PG ? 4 * kPrefillMaxPages : 0)];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8, V8>::LDS + (PG ? 4 * kPrefillMaxPages : 0)];
   int bh, w;
   if (p.order != ORDER_NONE) {
     // ranks follow workgroup ids (the dispatch order); each XCD takes every 8th
@@ -765,14 +874,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // the Q loads, so the two latencies overlap)
   const int ta = w, tb = p.n_qtiles - 1 - w;
   {
-    QTile<D, FP8, OUT_F32, PG> a(p, smem, bh, tb);
+    QTile<D, FP8, OUT_F32, PG, V8> a(p, smem, bh, tb);
     a.start_stream();
     a.load_q();
     a.loop();
     a.epilogue();
   }
   if (p.pair && ta != tb) {
-    QTile<D, FP8, OUT_F32, PG> b(p, smem, bh, ta);
+    QTile<D, FP8, OUT_F32, PG, V8> b(p, smem, bh, ta);
     b.start_stream();
     b.load_q();
     b.loop();
@@ -794,20 +903,21 @@ Params base_params(const void* q, const void* k, const void* v, void* o, float* 
   return p;
 }
 
-template <int D, bool FP8, bool OUT_F32, bool PG>
+template <int D, bool FP8, bool OUT_F32, bool PG, bool V8 = false>
 hipError_t launch_p(Params& p, int BH, hipStream_t stream) {
   p.units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   p.units = BH * p.units_per_bh;
   const int grid = round_up8(p.units);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32, PG>), dim3(grid), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32, PG, V8>), dim3(grid), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool FP8, bool OUT_F32>
+template <int D, bool FP8, bool OUT_F32, bool V8 = false>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   Params p = base_params(a.q, a.k, a.v, a.o, a.lse, a.N, a.scale);
   p.q_scale = a.q_scale;
   p.k_scale = a.k_scale;
+  p.v_scale = a.v_scale;
   p.doc = a.doc;
   p.mask = a.mask;
   p.window = a.window;
@@ -818,7 +928,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     p.groups = p.n_qtiles;
     p.per_group = a.BH;
   }
-  return launch_p<D, FP8, OUT_F32, false>(p, a.BH, stream);
+  return launch_p<D, FP8, OUT_F32, false, V8>(p, a.BH, stream);
 }
 
 template <int D, bool OUT_F32>
@@ -850,6 +960,9 @@ hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t stream) {
+  if (a.v8) {
+    return a.d == 64 ? launch_t<64, true, false, true>(a, stream) : launch_t<128, true, false, true>(a, stream);
+  }
   if (a.fp8) {
     return a.d == 64 ? launch_t<64, true, false>(a, stream) : launch_t<128, true, false>(a, stream);
   }

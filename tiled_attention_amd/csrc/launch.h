@@ -15,11 +15,12 @@ struct FwdArgs {
   float* lse;           // nullable
   const float* q_scale; // fp8 only: [BH, ceil(N/128)]
   const float* k_scale;
+  const float* v_scale; // all-fp8 path: V codes' power-of-two block scales (else null)
   const int32_t* doc;   // document masks: [num_docs + 1] start offsets
   int num_docs;
   int BH, N, d, mask, window;  // window clamped (clamp_window)
   float scale;
-  bool in_f32, out_f32, fp8;
+  bool in_f32, out_f32, fp8, v8;
 };
 
 // Prefill / cross-attention over a paged pool of 64-token pages.
@@ -70,7 +71,7 @@ hipError_t launch_fwd_paged(const PagedFwdArgs& a, hipStream_t stream);
 constexpr int kPrefillPageSize = 64;
 constexpr int kPrefillMaxPages = 4096;  // page ids of one list staged in LDS
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
-hipError_t launch_quant_fp8(const float* x, uint8_t* codes, float* scales, int BH, int N, int d,
+hipError_t launch_quant_fp8(const float* x, uint8_t* codes, float* scales, int BH, int N, int d, bool pow2,
                             hipStream_t stream);
 
 }  // namespace attn

@@ -3,7 +3,9 @@
 // "FlashAttention-3: Warp Specialization ...", "FP8 Block Quantization": each
 // block is divided by its own fp32 scale = absmax / 448 and cast to E4M3.
 // One workgroup per (block, head): pass 1 finds the block's absmax, pass 2
-// writes the codes. Divisions are IEEE fp32 (correctly rounded), so the codes
+// writes the codes. The power-of-two variant (for V in the all-fp8 path)
+// rounds the scale up to 2^k, the smallest power of two with absmax / 2^k <=
+// 448, so a matrix core can apply it as an exponent. Divisions are IEEE fp32 (correctly rounded), so the codes
 // are a pure function of the fp32 input; the rounding to E4M3 is done on the
 // fp32 bit pattern (nearest, ties to even, saturating at 448).
 #include "attn_common.h"
@@ -44,7 +46,7 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
 }
 
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
-                                                        float* __restrict__ scales, int N, int D, int nb) {
+                                                        float* __restrict__ scales, int N, int D, int nb, int pow2) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   const int bh = blockIdx.y;
@@ -62,7 +64,14 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const float* __restrict_
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = amax == 0.f ? 1.0f : amax / 448.0f;
+  float s = amax == 0.f ? 1.0f : amax / 448.0f;
+  if (pow2 && amax != 0.f) {
+    // amax = m * 2^e with m in [0.5, 1) and 448 = 0.875 * 2^9: the exact
+    // comparison of mantissas picks 2^(e-9) or 2^(e-8)
+    int e;
+    const float m = frexpf(amax, &e);
+    s = ldexpf(1.0f, max(m <= 0.875f ? e - 9 : e - 8, -127));
+  }
   uint32_t* cb = (uint32_t*)(codes + off);
   for (int i = threadIdx.x; i < cnt4; i += 256) {
     const float4 v = xb[i];
@@ -74,10 +83,11 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const float* __restrict_
 
 }  // namespace
 
-hipError_t launch_quant_fp8(const float* x, uint8_t* codes, float* scales, int BH, int N, int d,
+hipError_t launch_quant_fp8(const float* x, uint8_t* codes, float* scales, int BH, int N, int d, bool pow2,
                             hipStream_t stream) {
   const int nb = (N + QB - 1) / QB;
-  hipLaunchKernelGGL(quant_fp8_kernel, dim3(nb, BH), dim3(256), 0, stream, x, codes, scales, N, d, nb);
+  hipLaunchKernelGGL(quant_fp8_kernel, dim3(nb, BH), dim3(256), 0, stream, x, codes, scales, N, d, nb,
+                     pow2 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -105,6 +105,10 @@ WORKLOADS = {
                  n_seq=16, l_min=1024, l_max=8192, page_size=64, q_len=512),
     12: Workload(12, "paged_cross_bf16_s8_h32_d128_p64_q1024_32of1024pages", "paged_cross", H=32, d=128,
                  n_seq=8, page_size=64, q_len=1024, pool_pages=1024, pages_per_block=32, spare_pages=16),
+    # the fp8 causal shape with V in fp8 too (power-of-two block scales) and P
+    # rounded to fp8 for the second product
+    13: Workload(13, "fp8_full_causal_b1_h16_n16384_d128", "fp8_full", B=1, H=16, N=16384, d=128,
+                 mask="causal", outlier_p=0.01, outlier_scale=20.0),
 }
 
 
