@@ -166,7 +166,9 @@ struct Params {
 enum UnitOrder {
   ORDER_NONE = 0,    // unit u -> (bh, w) = (u / units_per_bh, u % units_per_bh), XCD-grouped
   ORDER_DOC = 1,     // groups = Q tiles, costed by the keys their documents span; per group: the heads
-  ORDER_SEQ = 2      // groups = sequences of a paged prefill, costed by length; per group: heads x units
+  ORDER_SEQ = 2,     // groups = sequences of a paged prefill, costed by length; per group: heads x units
+  ORDER_TILES = 3    // one Q tile per unit, tile-major from the last tile down (costs never fall with
+                     // the tile index for these masks), heads innermost so a head stays on one XCD
 };
 constexpr int kOrderMaxDocs = 8192;  // document offsets staged in LDS for the costing
 
@@ -857,7 +859,13 @@ template <int D, bool FP8, bool OUT_F32, bool PG, bool V8>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8, V8>::LDS + (PG ? 4 * kPrefillMaxPages : 0)];
   int bh, w;
-  if (p.order != ORDER_NONE) {
+  if (p.order == ORDER_TILES) {
+    const int u = blockIdx.x;
+    if (u >= p.units) return;
+    const int r = u / p.per_group;       // per_group = B*H
+    bh = u - r * p.per_group;
+    w = r;                               // tile n_qtiles - 1 - r
+  } else if (p.order != ORDER_NONE) {
     // ranks follow workgroup ids (the dispatch order); each XCD takes every 8th
     const int u = blockIdx.x;
     if (u >= p.units) return;
@@ -922,10 +930,18 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.mask = a.mask;
   p.window = a.window;
   p.nd = a.num_docs;
-  p.pair = (a.mask == MASK_CAUSAL || a.mask == MASK_PREFIX_LM) ? 1 : 0;
-  if (is_document(a.mask) && p.n_qtiles <= NT && a.num_docs + 1 <= kOrderMaxDocs) {
-    p.order = ORDER_DOC;
-    p.groups = p.n_qtiles;
+  if (is_document(a.mask)) {
+    if (p.n_qtiles <= NT && a.num_docs + 1 <= kOrderMaxDocs) {
+      p.order = ORDER_DOC;
+      p.groups = p.n_qtiles;
+      p.per_group = a.BH;
+    }
+  } else if (a.mask == MASK_CAUSAL || a.mask == MASK_PREFIX_LM) {
+    // Q tiles of rising cost: single tiles, costliest first, so a slot that
+    // frees early takes a cheap tile (a pair of tiles t and T-1-t per
+    // workgroup left one of the two workgroups of a CU running alone at the
+    // end: they share the CU unevenly)
+    p.order = ORDER_TILES;
     p.per_group = a.BH;
   }
   return launch_p<D, FP8, OUT_F32, false, V8>(p, a.BH, stream);
