@@ -108,7 +108,7 @@ def test_quant_rejects():
 def test_paged_rejects_and_workspace_size():
     lib = _lib.load()
     ws = lib.attn_decode_paged_workspace_size(64, 32, 128, 512, 16)
-    assert ws == 64 * 32 * 16 * (128 + 2) * 4            # 16 ranges of 32 pages per sequence
+    assert ws == 64 * 32 * 8 * (128 + 2) * 4             # 8 ranges of 64 pages per sequence
     assert lib.attn_decode_paged_workspace_size(64, 32, 128, 512, 64) == 0
     ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 16, 8, 20, 0.1, None, FAKE, 10 ** 9, None]
     assert lib.attn_decode_paged(*[None] + ok[1:]) == _lib.ATTN_ERR_INVALID_ARG

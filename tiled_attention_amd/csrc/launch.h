@@ -62,7 +62,7 @@ struct GatherArgs {
 };
 
 // Pages per split of the split-KV decode, and the resulting workspace size.
-constexpr int kDecodeSplitPages = 32;
+constexpr int kDecodeSplitPages = 64;
 size_t decode_workspace_bytes(int S, int H, int d, int max_pages);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
