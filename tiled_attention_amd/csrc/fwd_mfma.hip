@@ -257,6 +257,9 @@ struct QTile {
   int f_lo, f_hi;           // local tiles [f_lo, f_hi) are FULL for this wave
   size_t head;
   QFrag qf[QK_STEPS];
+  // Q as loaded: 16-byte pieces, two per k-step for fp8
+  static constexpr int QRAW = FP8 ? 2 * QK_STEPS : QK_STEPS;
+  i32x4 qraw[QRAW];
   float qscale;
   int kdma[KLD], vdma[VLD];
   int kread[QK_STEPS * (FP8 ? 2 : 1)];
@@ -419,21 +422,57 @@ struct QTile {
     l_run = 0.f;
   }
 
-  // Q fragments: lane (row l32, half hl) holds the k-slots of half hl. Not
-  // waited for here: the first MFMA that reads them waits.
+  // Q fragments: lane (row l32, half hl) holds the k-slots of half hl. The
+  // loads are issued before the tile stream's first DMAs and are not tracked
+  // by the compiler, so the loop's first wait can let the later prologue DMAs
+  // stay in flight (a compiler-inserted wait for Q would drain them all).
+  static __device__ __forceinline__ i32x4 gload16(const void* ptr) {
+    i32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(ptr) : "memory");
+    return r;
+  }
   __device__ __forceinline__ void load_q() {
     if constexpr (FP8) {
       const unsigned char* qp = (const unsigned char*)p.q + (head + qsrc) * D + 32 * hl;
 #pragma unroll
       for (int t = 0; t < QK_STEPS; ++t) {
-        const i32x4 a = *(const i32x4*)(qp + 64 * t);
-        const i32x4 b = *(const i32x4*)(qp + 64 * t + 16);
-        qf[t] = (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        qraw[2 * t] = gload16(qp + 64 * t);
+        qraw[2 * t + 1] = gload16(qp + 64 * t + 16);
       }
     } else {
       const __bf16* qp = (const __bf16*)p.q + (head + qsrc) * D + 8 * hl;
 #pragma unroll
-      for (int t = 0; t < QK_STEPS; ++t) qf[t] = *(const bf16x8*)(qp + 16 * t);
+      for (int t = 0; t < QK_STEPS; ++t) qraw[t] = gload16(qp + 16 * t);
+    }
+  }
+  // waits until at most N vector-memory operations of this wave are
+  // outstanding, then for every wave; the Q registers are operands, so no
+  // read of them is scheduled before the wait
+  template <int N>
+  __device__ __forceinline__ void q_landed() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    static_assert(QRAW == 2 || QRAW == 4 || QRAW == 8, "Q pieces");
+    if constexpr (QRAW == 2)
+      asm volatile("s_waitcnt vmcnt(%2)\n\ts_barrier" : "+v"(qraw[0]), "+v"(qraw[1]) : "n"(N) : "memory");
+    else if constexpr (QRAW == 4)
+      asm volatile("s_waitcnt vmcnt(%4)\n\ts_barrier"
+                   : "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3])
+                   : "n"(N)
+                   : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%8)\n\ts_barrier"
+                   : "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]), "+v"(qraw[4]), "+v"(qraw[5]),
+                     "+v"(qraw[6]), "+v"(qraw[7])
+                   : "n"(N)
+                   : "memory");
+#pragma unroll
+    for (int t = 0; t < QK_STEPS; ++t) {
+      if constexpr (FP8) {
+        const i32x4 a = qraw[2 * t], b = qraw[2 * t + 1];
+        qf[t] = (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      } else {
+        qf[t] = __builtin_bit_cast(bf16x8, qraw[t]);
+      }
     }
   }
 
@@ -755,12 +794,10 @@ struct QTile {
   __device__ __forceinline__ void loop() {
 #pragma unroll
     for (int e = 0; e < DE; ++e) oacc[e] = (f32x16){};
-    // The Q loads complete here (with the prologue DMA issued before them: the
-    // wait counter drains in order). A Q load still outstanding inside the
-    // loop would make the compiler's wait for it drain the K/V prefetch too.
-#pragma unroll
-    for (int t = 0; t < QK_STEPS; ++t) asm volatile("" ::"v"(qf[t]));
-    sync_tiles<0>();
+    // Q (issued first) and K_0 have landed once no more than the NS - 1
+    // later prologue batches are outstanding (the counter drains in order);
+    // those batches keep streaming under the first steps
+    q_landed<(NS - 1) * L>();
 #pragma unroll
     for (int q = 0; q < 4; ++q) P[1][q] = (bf16x8){};
     P8[1] = (i32x8){};
@@ -893,20 +930,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
   bh = __builtin_amdgcn_readfirstlane(bh);
   w = __builtin_amdgcn_readfirstlane(w);
-  // the longer Q tile first (its tile stream's first DMAs are issued before
-  // the Q loads, so the two latencies overlap)
+  // the longer Q tile first; Q is loaded before the tile stream's first DMAs,
+  // so the two latencies overlap
   const int ta = w, tb = p.n_qtiles - 1 - w;
   {
     QTile<D, FP8, OUT_F32, PG, V8> a(p, smem, bh, tb);
-    a.start_stream();
     a.load_q();
+    a.start_stream();
     a.loop();
     a.epilogue();
   }
   if (p.pair && ta != tb) {
     QTile<D, FP8, OUT_F32, PG, V8> b(p, smem, bh, ta);
-    b.start_stream();
     b.load_q();
+    b.start_stream();
     b.loop();
     b.epilogue();
   }
