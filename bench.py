@@ -212,8 +212,8 @@ class Paged:
 
 
 class PagedPrefill:
-    """attn_prefill_paged over 64-token pages; also times the page gather a
-    two-stage (gather, then attend) route would add."""
+    """attn_prefill_paged over a paged pool (16- or 64-token pages); also times
+    the page gather a two-stage (gather, then attend) route would add."""
 
     def __init__(self, key, seed):
         import torch
@@ -429,7 +429,7 @@ def main():
     if not args.only_main:
         others = {}
         for key, reps in ((1, 200), (3, 20), (4, 20), (5, 20), (6, 20), (7, 20), (8, 10), (9, 20), (10, 20),
-                          (11, 20), (12, 20), (13, 20)):
+                          (11, 20), (12, 20), (13, 20), (14, 20)):
             log(f"bench: workload {key}")
             o = make(key)
             avg, med, mn = event_time_ms(o.step, reps)

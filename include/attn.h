@@ -42,7 +42,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, misalignment, bad enum, window out of range */
-  ATTN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d = 96, page_size = 64) */
+  ATTN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d = 96, 64-token pages for the decode) */
   ATTN_ERR_WORKSPACE = 3,    /* workspace smaller than the size query returns */
   ATTN_ERR_LAUNCH = 4        /* the HIP runtime reported a launch failure */
 } attn_status;
@@ -212,18 +212,20 @@ attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_p
  * attn_prefill_paged -- causal prefill over a paged KV cache ("Optimizing
  * Triton kernels ...", Pattern C, its prefix-caching use), with the page
  * gather fused into the attention's tile loads instead of a separate
- * gather-then-attend pass.
+ * gather-then-attend pass. It reads the decode's 16-token pool as well as a
+ * 64-token one.
  *   The last q_len positions of every sequence are the query rows: row i of
  *   sequence s sits at position seq_lens[s] - q_len + i and sees the keys at
  *   positions 0 .. that position (the new rows' own K/V already in the pool).
  *   q, o : [S, H, q_len, d]; q bf16, o of out_dtype (ATTN_BF16 or ATTN_F32).
- *   k_pool, v_pool : [num_pages, H, page_size, d] bf16; page_size must be 64
- *            (one page of one head is one 64-key tile).
+ *   k_pool, v_pool : [num_pages, H, page_size, d] bf16; page_size 64 (one
+ *            page of one head is one 64-key tile) or 16 (the decode's pages,
+ *            four per tile); any other size -> ATTN_ERR_UNSUPPORTED.
  *   block_table : [S, max_pages] int32 (device), as for attn_decode_paged.
- *   seq_lens : [S] int32 (device), q_len <= seq_lens[s] <= max_pages * 64.
+ *   seq_lens : [S] int32 (device), q_len <= seq_lens[s] <= max_pages * page_size.
  *   max_pages <= 4096 (a list is staged on chip). lse : NULL or [S, H, q_len] fp32.
  * The device contents (page ids, lengths) are the caller's contract and are
- * not checked: lengths are clamped to [0, max_pages * 64] and page ids into
+ * not checked: lengths are clamped to [0, max_pages * page_size] and page ids into
  * [0, num_pages), so other contents give unspecified results but no access
  * outside the buffers.
  */
@@ -239,9 +241,9 @@ attn_status attn_prefill_paged(const void* q, const void* k_pool, const void* v_
  * retrieval). Query block b of sequence s, rows 128b .. 128b + 127 of q[s],
  * attends with no mask to the first kv_lens[s, b] tokens of the
  * concatenation of pages page_table[s, b, 0], page_table[s, b, 1], ...
- *   q, o, pools, page_size (64), max_pages (<= 4096) as for attn_prefill_paged.
+ *   q, o, pools, page_size (16 or 64), max_pages (<= 4096) as for attn_prefill_paged.
  *   page_table : [S, ceil(q_len / 128), max_pages] int32 (device).
- *   kv_lens : [S, ceil(q_len / 128)] int32 (device), 0 <= kv_lens <= max_pages * 64;
+ *   kv_lens : [S, ceil(q_len / 128)] int32 (device), 0 <= kv_lens <= max_pages * page_size;
  *            a block with no key gets O = 0 and LSE = -inf.
  * Device contents are handled as for attn_prefill_paged.
  */
@@ -256,7 +258,7 @@ attn_status attn_cross_paged(const void* q, const void* k_pool, const void* v_po
  *   k_out[s, h, t, :] = k_pool[block_table[s, t / page_size], h, t % page_size, :]
  * (same for v) for t < seq_lens[s]. k_out, v_out: [S, H, max_pages*page_size, d]
  * of `dtype` (ATTN_BF16 or ATTN_F32, element size only); rows t >= seq_lens[s]
- * are left untouched. page_size 16 (the decode's pages) or 64 (the prefill's).
+ * are left untouched. page_size 16 (the decode's pages) or 64.
  */
 attn_status attn_gather_paged(const void* k_pool, const void* v_pool,
                               const int32_t* block_table, const int32_t* seq_lens,

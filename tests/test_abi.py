@@ -137,8 +137,11 @@ def test_paged_prefill_rejects(name):
     for i in (0, 1, 2, 3, 4, 5):
         bad = list(ok); bad[i] = None
         assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
-    bad = list(ok); bad[10] = 16
-    assert f(*bad) == _lib.ATTN_ERR_UNSUPPORTED          # 16-token pages: the decode's, not these
+    for page in (8, 32, 128):
+        bad = list(ok); bad[10] = page
+        assert f(*bad) == _lib.ATTN_ERR_UNSUPPORTED      # pages of 16 or 64 tokens only
+    bad = list(ok); bad[10] = 0
+    assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
     bad = list(ok); bad[11] = 4097
     assert f(*bad) == _lib.ATTN_ERR_UNSUPPORTED          # list longer than the on-chip staging
     bad = list(ok); bad[9] = 96

@@ -1,8 +1,9 @@
 """GPU parity of the fused paged prefill and block-sparse paged
 cross-attention ("Optimizing Triton kernels for custom attention patterns on
 H100", Pattern C) against the oracle, element by element on small ragged
-cases and on sampled rows at the full workload sizes. The pools hold NaN in
-every row no sequence or list owns, so a read past a list shows up."""
+cases (64-token pages, and the decode's 16-token pages, four to a K tile) and
+on sampled rows at the full workload sizes. The pools hold NaN in every row
+no sequence or list owns, so a read past a list shows up."""
 
 import math
 
@@ -37,14 +38,15 @@ PREFILL = [(3, 2, 1, 128, 1, 200), (2, 3, 100, 64, 100, 700), (4, 2, 300, 128, 3
 
 @pytest.mark.parametrize("case", PREFILL, ids=lambda c: "-".join(map(str, c)))
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_prefill_paged_small_elementwise(case, out):
+@pytest.mark.parametrize("page", [64, 16])
+def test_prefill_paged_small_elementwise(case, out, page):
     S, H, q_len, d, l_min, l_max = case
-    say(f"paged prefill {case} out={out}")
-    inp = wl.paged_inputs(S, H, d, l_min, l_max, seed=41 + q_len + d, page_size=64, spare=5, q_rows=q_len)
+    say(f"paged prefill {case} out={out} page={page}")
+    inp = wl.paged_inputs(S, H, d, l_min, l_max, seed=41 + q_len + d, page_size=page, spare=5, q_rows=q_len)
     scale = 1.0 / math.sqrt(d)
     o, lse = _prefill(inp, q_len, torch.float32 if out == "f32" else torch.bfloat16, scale)
     ref, ref_lse = oracle.prefill(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
-                                  inp.block_table.numpy(), inp.seq_lens.numpy(), scale, page_size=64)
+                                  inp.block_table.numpy(), inp.seq_lens.numpy(), scale, page_size=page)
     check_close(to_np(o), ref, out == "bf16", what=str(case))
     assert np.max(np.abs(to_np(lse) - ref_lse)) <= LSE_TOL_MFMA
 
@@ -66,16 +68,17 @@ CROSS = [(2, 2, 300, 64, 9, 4), (1, 3, 128, 128, 40, 17), (3, 1, 1, 128, 5, 1), 
 
 @pytest.mark.parametrize("case", CROSS, ids=lambda c: "-".join(map(str, c)))
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_cross_paged_small_elementwise(case, out):
+@pytest.mark.parametrize("page", [64, 16])
+def test_cross_paged_small_elementwise(case, out, page):
     S, H, q_len, d, pool, per = case
-    say(f"paged cross {case} out={out}")
-    inp = wl.paged_cross_inputs(S, H, d, q_len, pool, per, seed=43 + q_len, page_size=64, spare=3)
+    say(f"paged cross {case} out={out} page={page}")
+    inp = wl.paged_cross_inputs(S, H, d, q_len, pool, per, seed=43 + q_len, page_size=page, spare=3)
     if S * (-(-q_len // 128)) > 1:
         inp.kv_lens[0, -1] = 0                 # one block with no keys: O = 0, LSE = -inf
     scale = 1.0 / math.sqrt(d)
     o, lse = _cross(inp, torch.float32 if out == "f32" else torch.bfloat16, scale)
     ref, ref_lse = oracle.cross(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
-                                inp.page_table.numpy(), inp.kv_lens.numpy(), scale, page_size=64)
+                                inp.page_table.numpy(), inp.kv_lens.numpy(), scale, page_size=page)
     check_close(to_np(o), ref, out == "bf16", what=str(case))
     got_lse = to_np(lse)
     live = np.isfinite(ref_lse)
@@ -83,9 +86,10 @@ def test_cross_paged_small_elementwise(case, out):
     assert np.max(np.abs(got_lse[live] - ref_lse[live])) <= LSE_TOL_MFMA
 
 
-def test_prefill_paged_full_size_sampled():
-    w = wl.WORKLOADS[11]
-    seed = wl.default_seed(11)
+@pytest.mark.parametrize("key", [11, 14])
+def test_prefill_paged_full_size_sampled(key):
+    w = wl.WORKLOADS[key]
+    seed = wl.default_seed(key)
     say(f"{w.name}: generating inputs (seed {seed})")
     inp = wl.paged_inputs(w.n_seq, w.H, w.d, w.l_min, w.l_max, seed=seed, page_size=w.page_size,
                           spare=w.spare_pages, q_rows=w.q_len)
@@ -98,8 +102,8 @@ def test_prefill_paged_full_size_sampled():
     for s, h in [(0, 0), (7, 31), (15, 12)]:
         rows = sample_rows(w.q_len, seed + s)
         L = int(lens[s])
-        k = oracle.gather(kp, table[s:s + 1], lens[s:s + 1], page_size=64)[0][h]
-        v = oracle.gather(vp, table[s:s + 1], lens[s:s + 1], page_size=64)[0][h]
+        k = oracle.gather(kp, table[s:s + 1], lens[s:s + 1], page_size=w.page_size)[0][h]
+        v = oracle.gather(vp, table[s:s + 1], lens[s:s + 1], page_size=w.page_size)[0][h]
         ref, ref_lse = oracle.attention(wl.bf16_to_f64(inp.q[s, h]), k, v, w.scale, "causal", rows=rows,
                                         q_pos_offset=L - w.q_len)
         check_close(to_np(o32[s, h][rows]), ref, False, what=f"{w.name} f32 {(s, h)}")
@@ -133,7 +137,7 @@ def test_cross_paged_full_size_sampled():
 
 
 def test_prefill_paged_one_row_matches_decode():
-    """q_len = 1 is a decode: the fused prefill kernel and the split-KV decode agree."""
+    """q_len = 1 is a decode: the fused prefill kernel and the decode oracle agree."""
     inp = wl.paged_inputs(4, 2, 128, 1, 3000, seed=47, page_size=64, spare=2, q_rows=1)
     o, _ = _prefill(inp, 1, torch.float32, 1 / math.sqrt(128))
     ref, _ = oracle.decode(wl.bf16_to_f64(inp.q[:, :, 0]), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
@@ -141,13 +145,36 @@ def test_prefill_paged_one_row_matches_decode():
     check_close(to_np(o[:, :, 0]), ref, False, what="q_len=1")
 
 
+def test_prefill_and_decode_share_a_16_token_pool():
+    """One pool of the decode's 16-token pages serves both paths: the fused
+    prefill's last row of each sequence and the decode of that row both match
+    the decode oracle (the prefill rounds P to bf16, the decode does not)."""
+    S, H, d = 5, 4, 128
+    inp = wl.paged_inputs(S, H, d, 200, 5000, seed=53, page_size=16, spare=7, q_rows=96)
+    scale = 1 / math.sqrt(d)
+    o, lse = _prefill(inp, 96, torch.float32, scale)
+    q_last = inp.q[:, :, -1].contiguous().cuda()
+    od = torch.full((S, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")   # the decode writes bf16
+    lsed = torch.full((S, H), float("nan"), dtype=torch.float32, device="cuda")
+    A.attn_decode_paged(q_last, inp.k_pool.cuda(), inp.v_pool.cuda(), inp.block_table.cuda(), inp.seq_lens.cuda(),
+                        od, scale, lse=lsed)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode(wl.bf16_to_f64(inp.q[:, :, -1]), inp.k_pool.float().numpy(),
+                                 inp.v_pool.float().numpy(), inp.block_table.numpy(), inp.seq_lens.numpy(), scale,
+                                 page_size=16)
+    check_close(to_np(o[:, :, -1]), ref, False, what="prefill's last row on the shared pool")
+    check_close(to_np(od), ref, True, what="decode on the shared pool")
+    assert np.max(np.abs(to_np(lse[:, :, -1]) - ref_lse)) <= LSE_TOL_MFMA
+    assert np.max(np.abs(to_np(lsed) - ref_lse)) <= LSE_TOL_MFMA
+
+
 def test_paged_prefill_rejects():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
     o = torch.full_like(q, 3.0)
-    pool16 = torch.zeros(4, 1, 16, 64, dtype=torch.bfloat16, device="cuda")
+    pool32 = torch.zeros(4, 1, 32, 64, dtype=torch.bfloat16, device="cuda")
     table = torch.zeros(1, 4, dtype=torch.int32, device="cuda")
     lens = torch.full((1,), 8, dtype=torch.int32, device="cuda")
-    with pytest.raises(ValueError):            # 16-token pages: unsupported here
-        A.attn_prefill_paged(q, pool16, pool16, table, lens, o, 0.125)
+    with pytest.raises(ValueError):            # 32-token pages: unsupported
+        A.attn_prefill_paged(q, pool32, pool32, table, lens, o, 0.125)
     torch.cuda.synchronize()
     assert torch.all(o == 3.0)

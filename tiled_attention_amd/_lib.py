@@ -188,6 +188,8 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, scale, worksp
                       stream=None):
     """Single-token decode over a paged KV pool; workspace None -> one pass per (sequence, head)."""
     _dev(q, k_pool, v_pool, block_table, seq_lens, o, workspace, lse)
+    import torch
+    _require(o.dtype == torch.bfloat16 and o.shape == q.shape, "o must be bf16 and shaped like q")
     S, H, d = q.shape
     num_pages, _, page_size, _ = k_pool.shape
     max_pages = block_table.shape[1]
@@ -210,7 +212,7 @@ def _paged_fwd(fn, q, k_pool, v_pool, table, lens, o, scale, lse, stream):
 
 
 def attn_prefill_paged(q, k_pool, v_pool, block_table, seq_lens, o, scale, lse=None, stream=None):
-    """Causal prefill of the last q_len positions of each paged sequence (64-token pages)."""
+    """Causal prefill of the last q_len positions of each paged sequence (16- or 64-token pages)."""
     return _paged_fwd(load().attn_prefill_paged, q, k_pool, v_pool, block_table, seq_lens, o, scale, lse, stream)
 
 

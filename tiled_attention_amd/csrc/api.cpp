@@ -211,7 +211,7 @@ attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_p
   return launched(attn::launch_decode(a, (hipStream_t)stream));
 }
 
-// Shared checks of the two 64-token-page prefill entry points.
+// Shared checks of the two paged prefill entry points (16- or 64-token pages).
 static attn_status paged_fwd(const void* q, const void* k_pool, const void* v_pool, const int32_t* table,
                              const int32_t* lens, void* o, int S, int H, int q_len, int d, int page_size,
                              int max_pages, int num_pages, attn_dtype out_dtype, float scale, float* lse,
@@ -227,7 +227,9 @@ static attn_status paged_fwd(const void* q, const void* k_pool, const void* v_po
   if (st != ATTN_OK) return st;
   const int qb = (q_len + 127) / 128;
   if ((long long)S * qb * max_pages >= (1LL << 31)) return ATTN_ERR_INVALID_ARG;
-  if (page_size != attn::kPrefillPageSize || max_pages > attn::kPrefillMaxPages) return ATTN_ERR_UNSUPPORTED;
+  if (page_size != attn::kPrefillPageSize && page_size != attn::kPrefillSmallPage) return ATTN_ERR_UNSUPPORTED;
+  if (max_pages > attn::kPrefillMaxPages) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)num_pages * H * page_size * d >= (1LL << 40)) return ATTN_ERR_INVALID_ARG;
   attn::PagedFwdArgs a{};
   a.q = q;
   a.k_pool = k_pool;
@@ -242,6 +244,7 @@ static attn_status paged_fwd(const void* q, const void* k_pool, const void* v_po
   a.d = d;
   a.max_pages = max_pages;
   a.num_pages = num_pages;
+  a.page_size = page_size;
   a.table_stride_s = causal ? max_pages : qb * max_pages;
   a.table_stride_b = causal ? 0 : max_pages;
   a.lens_stride_s = causal ? 1 : qb;

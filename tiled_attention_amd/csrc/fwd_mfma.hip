@@ -50,15 +50,18 @@
 //    H100", Patterns A and B: loop bounds, edge-only masking, document bounds
 //    found by a search of the document offsets). The mask kind is a run-time
 //    value: it only changes this set-up.
-//  * Causal and prefix-LM: a workgroup takes Q tiles t and T-1-t so all carry
-//    about equal work; workgroup ids are mapped so that a head's tiles share
-//    an XCD (its L2).
+//  * Causal and prefix-LM: one Q tile per workgroup, dispatched costliest
+//    first (tile-major from the last tile down, heads innermost, so that a
+//    head's tiles share an XCD and its L2).
 //  * Paged K/V ("Optimizing Triton kernels ...", Pattern C, fused instead of
 //    gather-then-attend): with 64-token pages of a [pages, H, 64, d] pool one
 //    page of one head is exactly one K (or V) tile, contiguous, so the same
-//    LDS DMA fetches it from its page's address. A Q tile's page list is
-//    staged in LDS once; each issue reads its page id from there and clips
-//    the descriptor at the list's last valid token (later rows load as zeros).
+//    LDS DMA fetches it from its page's address. With 16-token pages a tile
+//    spans four pages; the rows of one DMA instruction lie in one of them, so
+//    each instruction takes its own page's descriptor. A Q tile's page list
+//    is staged in LDS once; each issue reads its page ids from there and
+//    clips the descriptors at the list's last valid token (later rows load as
+//    zeros).
 #include <type_traits>
 #include <utility>
 
@@ -150,13 +153,14 @@ struct Params {
   const float* v_scale;
   const int32_t* doc;
   int N, mask, window, nd, n_qtiles, units_per_bh, units, pair, nsb;
-  // paged K/V: k, v are [pool pages, H, 64, d] pools; (sequence s, query
-  // block b) reads the page list pg_table + s * pg_stride_s + b * pg_stride_b
-  // and its length pg_lens[s * len_stride_s + b * len_stride_b] (the sequence
-  // length when pg_causal, else the number of keys)
+  // paged K/V: k, v are [pool pages, H, pg_page, d] pools (pg_page 16 or
+  // 64 tokens); (sequence s, query block b) reads the page list
+  // pg_table + s * pg_stride_s + b * pg_stride_b and its length
+  // pg_lens[s * len_stride_s + b * len_stride_b] (the sequence length when
+  // pg_causal, else the number of keys)
   const int32_t* pg_table;
   const int32_t* pg_lens;
-  int H, pg_stride_s, pg_stride_b, len_stride_s, len_stride_b, pg_max, pg_pool, pg_causal;
+  int H, pg_stride_s, pg_stride_b, len_stride_s, len_stride_b, pg_max, pg_pool, pg_causal, pg_page;
   // heaviest-first dispatch (order != ORDER_NONE): units come in `groups`
   // groups of `per_group` equal-cost units
   int order, groups, per_group;
@@ -228,7 +232,7 @@ struct TileStream {
   }
 };
 
-template <int D, bool FP8, bool OUT_F32, bool PG, bool V8>
+template <int D, bool FP8, bool OUT_F32, int PG, bool V8>
 struct QTile {
   static_assert(!(PG && FP8), "paged K/V is bf16");
   static_assert(!V8 || FP8, "fp8 V comes with fp8 Q and K");
@@ -306,7 +310,7 @@ struct QTile {
       const int s = bh / p.H;
       pg_h = bh - s * p.H;
       const int32_t* list = p.pg_table + (size_t)s * p.pg_stride_s + (size_t)qt * p.pg_stride_b;
-      pg_len = min(max(p.pg_lens[s * p.len_stride_s + qt * p.len_stride_b], 0), p.pg_max * BN);
+      pg_len = min(max(p.pg_lens[s * p.len_stride_s + qt * p.len_stride_b], 0), p.pg_max * p.pg_page);
       const int pos0 = pg_len - N;
       auto span = [&](int r) -> KeySpan { return {0, p.pg_causal ? min(pg_len - 1, pos0 + r) : pg_len - 1}; };
       sp.lane = span(qsrc);
@@ -317,9 +321,11 @@ struct QTile {
       t_lo = 0;
       NK = sp.tile_last.hi >= 0 ? sp.tile_last.hi / BN + 1 : 0;
       // stage the page ids of the tiles this Q tile visits (clamped into the
-      // pool); NK <= pg_max <= kPrefillMaxPages
+      // pool): one per tile, or four with 16-token pages, at most the list's
+      // pg_max <= kPrefillMaxPages entries
       int* ids = (int*)(smem + C::LDS);
-      for (int i = tid; i < NK; i += NT) ids[i] = min(max(list[i], 0), p.pg_pool - 1);
+      const int n_ids = min(NK * (BN / p.pg_page), p.pg_max);
+      for (int i = tid; i < n_ids; i += NT) ids[i] = min(max(list[i], 0), p.pg_pool - 1);
       __syncthreads();
       pg_ids = ids;
       pool_k = (uint64_t)(uintptr_t)p.k;
@@ -489,9 +495,36 @@ struct QTile {
                    __builtin_amdgcn_readfirstlane(rows * row_bytes), kBufferFlags};
   }
 
+  // 16-token pages: a tile spans four pages, and each DMA instruction's rows
+  // (1024 bytes, at most 16 rows) lie in one of them, so every instruction
+  // takes the descriptor of its own page (rows clipped at the list's length)
+  // and an offset within that page
+  template <int ROWB, int NLD>
+  __device__ __forceinline__ void issue_paged16(uint64_t pool, int j, uint32_t lds, const int (&off)[NLD]) const {
+    static_assert(1024 / ROWB <= 16, "a DMA instruction spans one 16-row page");
+    // ids 4j .. 4j + 3 (16-byte aligned); entries past the staged ones only
+    // reach pages with no rows to load
+    const int jc = max(min(j, NK - 1), 0);
+    const i32x4 q4 = *(const i32x4*)(pg_ids + 4 * jc);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int pi = (((u * NW + wave) * 1024) / ROWB) >> 4;   // page of the tile, scalar
+      const int pid = __builtin_amdgcn_readfirstlane(pi == 0 ? q4[0] : pi == 1 ? q4[1] : pi == 2 ? q4[2] : q4[3]);
+      const uint64_t base = pool + ((uint64_t)pid * p.H + pg_h) * (uint64_t)(16 * ROWB);
+      const int rows = min(max(pg_len - (j * BN + 16 * pi), 0), 16);
+      const i32x4 rs = {__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                        __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32)),
+                        __builtin_amdgcn_readfirstlane(rows * ROWB), kBufferFlags};
+      dma16(lds + u * NW * 1024, off[u] & (16 * ROWB - 1), rs);
+    }
+  }
+
   template <int SLOT>
   __device__ __forceinline__ void issue_k() {
-    if constexpr (PG) {
+    if constexpr (PG == kPrefillSmallPage) {
+      issue_paged16<KROW, KLD>(pool_k, k_next++, lds_k + SLOT * C::K_SLOT, kdma);
+      return;
+    } else if constexpr (PG) {
       const i32x4 rs = page_rsrc(pool_k, k_next++, C::K_SLOT, KROW);
 #pragma unroll
       for (int u = 0; u < KLD; ++u) dma16(lds_k + SLOT * C::K_SLOT + u * NW * 1024, kdma[u], rs);
@@ -505,7 +538,10 @@ struct QTile {
   }
   template <int SLOT>
   __device__ __forceinline__ void issue_v() {
-    if constexpr (PG) {
+    if constexpr (PG == kPrefillSmallPage) {
+      issue_paged16<VROW, VLD>(pool_v, v_next++, lds_v + SLOT * C::V_SLOT, vdma);
+      return;
+    } else if constexpr (PG) {
       const i32x4 rs = page_rsrc(pool_v, v_next++, C::V_SLOT, VROW);
 #pragma unroll
       for (int u = 0; u < VLD; ++u) dma16(lds_v + SLOT * C::V_SLOT + u * NW * 1024, vdma[u], rs);
@@ -878,7 +914,7 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
       const KeySpan l = doc_span(causal, offs[d], offs[d + 1], p.N, m1 - 1);
       c = l.hi / BN - f.lo / BN + 1;
     } else {
-      c = min(max(p.pg_lens[tid], 0), p.pg_max * BN);
+      c = min(max(p.pg_lens[tid], 0), p.pg_max * p.pg_page);
     }
     cost[tid] = c;
   }
@@ -907,7 +943,7 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
   }
 }
 
-template <int D, bool FP8, bool OUT_F32, bool PG, bool V8>
+template <int D, bool FP8, bool OUT_F32, int PG, bool V8>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8, V8>::LDS + (PG ? 4 * kPrefillMaxPages : 0)];
   int bh, w;
@@ -963,7 +999,7 @@ Params base_params(const void* q, const void* k, const void* v, void* o, float* 
   return p;
 }
 
-template <int D, bool FP8, bool OUT_F32, bool PG, bool V8 = false>
+template <int D, bool FP8, bool OUT_F32, int PG, bool V8 = false>
 hipError_t launch_p(Params& p, int BH, hipStream_t stream) {
   p.units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   p.units = BH * p.units_per_bh;
@@ -1012,6 +1048,7 @@ hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
   p.pg_max = a.max_pages;
   p.pg_pool = a.num_pages;
   p.pg_causal = a.causal ? 1 : 0;
+  p.pg_page = a.page_size;
   p.pair = p.pg_causal;
   const int units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   // cross-attention lists keep the natural order: ranking them (by length)
@@ -1022,7 +1059,8 @@ hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
     p.groups = a.S;
     p.per_group = a.H * units_per_bh;
   }
-  return launch_p<D, false, OUT_F32, true>(p, a.S * a.H, stream);
+  if (a.page_size == kPrefillSmallPage) return launch_p<D, false, OUT_F32, kPrefillSmallPage>(p, a.S * a.H, stream);
+  return launch_p<D, false, OUT_F32, kPrefillPageSize>(p, a.S * a.H, stream);
 }
 
 }  // namespace

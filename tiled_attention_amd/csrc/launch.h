@@ -26,13 +26,13 @@ struct FwdArgs {
 // Prefill / cross-attention over a paged pool of 64-token pages.
 struct PagedFwdArgs {
   const void* q;        // [S, H, q_len, d] bf16
-  const void* k_pool;   // [num_pages, H, 64, d] bf16
+  const void* k_pool;   // [num_pages, H, page_size, d] bf16
   const void* v_pool;
   void* o;
   float* lse;           // nullable
   const int32_t* table; // page lists (device)
   const int32_t* lens;  // list lengths (device)
-  int S, H, q_len, d, max_pages, num_pages;
+  int S, H, q_len, d, max_pages, num_pages, page_size;   // page_size 16 or 64
   int table_stride_s, table_stride_b, lens_stride_s, lens_stride_b;
   bool causal, out_f32;
   float scale;
@@ -68,7 +68,8 @@ size_t decode_workspace_bytes(int S, int H, int d, int max_pages);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_fwd_paged(const PagedFwdArgs& a, hipStream_t stream);
-constexpr int kPrefillPageSize = 64;
+constexpr int kPrefillPageSize = 64;     // one page of one head is one 64-key tile
+constexpr int kPrefillSmallPage = 16;    // the decode's pages: four per tile
 constexpr int kPrefillMaxPages = 4096;  // page ids of one list staged in LDS
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_quant_fp8(const float* x, uint8_t* codes, float* scales, int BH, int N, int d, bool pow2,

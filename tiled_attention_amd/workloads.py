@@ -109,6 +109,9 @@ WORKLOADS = {
     # rounded to fp8 for the second product
     13: Workload(13, "fp8_full_causal_b1_h16_n16384_d128", "fp8_full", B=1, H=16, N=16384, d=128,
                  mask="causal", outlier_p=0.01, outlier_scale=20.0),
+    # the paged prefill of workload 11 over the decode's 16-token pages
+    14: Workload(14, "paged_prefill_bf16_s16_h32_d128_p16_q512_l1024to8192", "paged_prefill", H=32, d=128,
+                 n_seq=16, l_min=1024, l_max=8192, page_size=16, q_len=512),
 }
 
 
