@@ -764,6 +764,15 @@ struct QTile {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
+    // P is converted before the test below, not sunk past its branch: the
+    // conversions then issue while the sum's add tree completes (1-3% at
+    // d = 64; the bf16 d = 128 kernels would spill the extra live values)
+    if constexpr (V8) {
+      asm volatile("" ::"v"(P8[B]));
+    } else if constexpr (D == 64) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) asm volatile("" ::"v"(P[B][q]));
+    }
     // a lane without a reference yet, or a tile sum past the limit, moves it
     // (before P V of the tile, which the next step issues)
     if (__builtin_expect(__any(!(psum <= limit)), 0)) rebase<B>(c, psum);
