@@ -191,7 +191,7 @@ class Paged:
         self.kp, self.vp = inp.k_pool.cuda(), inp.v_pool.cuda()
         self.bt, self.lens = inp.block_table.cuda(), inp.seq_lens.cuda()
         self.o = torch.empty(self.q.shape, dtype=torch.bfloat16, device="cuda")
-        nbytes = A.attn_decode_paged_workspace_size(w.n_seq, w.H, w.d, self.bt.shape[1])
+        nbytes = A.attn_decode_paged_workspace_size(w.n_seq, w.H, w.d, self.bt.shape[1], w.page_size)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         lens = inp.seq_lens.numpy().astype(int)
         self.tokens = int(lens.sum())
@@ -431,7 +431,7 @@ def main():
     if not args.only_main:
         others = {}
         for key, reps in ((1, 200), (3, 20), (4, 20), (5, 20), (6, 20), (7, 20), (8, 10), (9, 20), (10, 20),
-                          (11, 20), (12, 20), (13, 20), (14, 20)):
+                          (11, 20), (12, 20), (13, 20), (14, 20), (15, 20)):
             log(f"bench: workload {key}")
             o = make(key)
             avg, med, mn = event_time_ms(o.step, reps)

@@ -42,7 +42,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,  /* null pointer, size <= 0, misalignment, bad enum, window out of range */
-  ATTN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d = 96, 64-token pages for the decode) */
+  ATTN_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d = 96, 32-token pages) */
   ATTN_ERR_WORKSPACE = 3,    /* workspace smaller than the size query returns */
   ATTN_ERR_LAUNCH = 4        /* the HIP runtime reported a launch failure */
 } attn_status;
@@ -182,10 +182,13 @@ attn_status attn_quant_fp8_block_pow2(const float* x, uint8_t* codes, float* sca
  *   block_table    : [S, max_pages] int32 (device); token t of sequence s is
  *                    in page block_table[s, t / page_size], row t % page_size.
  *                    Entries at or past ceil(seq_lens[s] / page_size) are
- *                    never read. Page ids must lie in [0, num_pages): they
- *                    are not checked on the device (caller's contract).
+ *                    never read. Page ids must lie in [0, num_pages).
  *   seq_lens       : [S] int32 (device), 1 <= seq_lens[s] <= max_pages*page_size.
- *   page_size must be 16 for the decode (the gather also takes 64).
+ *   page_size      : 16 or 64 tokens (other sizes -> ATTN_ERR_UNSUPPORTED).
+ * The device contents are the caller's contract and are not checked: the
+ * kernels clamp page ids into [0, num_pages) (and the decode clamps lengths
+ * into [0, max_pages * page_size]), so other contents give unspecified
+ * results but no access outside the buffers.
  */
 
 /* Bytes of workspace attn_decode_paged uses to split long sequences. */

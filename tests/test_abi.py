@@ -109,11 +109,15 @@ def test_paged_rejects_and_workspace_size():
     lib = _lib.load()
     ws = lib.attn_decode_paged_workspace_size(64, 32, 128, 512, 16)
     assert ws == 64 * 32 * 8 * (128 + 2) * 4             # 8 ranges of 64 pages per sequence
-    assert lib.attn_decode_paged_workspace_size(64, 32, 128, 512, 64) == 0
+    # 64-token pages: four 16-token units each, so four times the ranges per table row
+    assert lib.attn_decode_paged_workspace_size(64, 32, 128, 128, 64) == ws
+    assert lib.attn_decode_paged_workspace_size(64, 32, 128, 512, 32) == 0
     ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 16, 8, 20, 0.1, None, FAKE, 10 ** 9, None]
     assert lib.attn_decode_paged(*[None] + ok[1:]) == _lib.ATTN_ERR_INVALID_ARG
-    bad = list(ok); bad[9] = 64
+    bad = list(ok); bad[9] = 32
     assert lib.attn_decode_paged(*bad) == _lib.ATTN_ERR_UNSUPPORTED
+    bad = list(ok); bad[9] = 64; bad[15] = lib.attn_decode_paged_workspace_size(2, 4, 128, 8, 64) - 1
+    assert lib.attn_decode_paged(*bad) == _lib.ATTN_ERR_WORKSPACE
     bad = list(ok); bad[15] = 16
     assert lib.attn_decode_paged(*bad) == _lib.ATTN_ERR_WORKSPACE
     bad = list(ok); bad[14] = FAKE_MIS

@@ -22,7 +22,7 @@ def _decode(inp, scale, use_ws):
     lse = torch.full((S, H), float("nan"), dtype=torch.float32, device="cuda")
     ws = None
     if use_ws:
-        nbytes = A.attn_decode_paged_workspace_size(S, H, d, bt.shape[1])
+        nbytes = A.attn_decode_paged_workspace_size(S, H, d, bt.shape[1], kp.shape[2])
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     A.attn_decode_paged(q, kp, vp, bt, lens, o, scale, workspace=ws, lse=lse)
     torch.cuda.synchronize()
@@ -32,16 +32,19 @@ def _decode(inp, scale, use_ws):
 def _oracle_decode(inp, scale, seqs=None):
     seqs = list(range(inp.q.shape[0])) if seqs is None else seqs
     o, lse = oracle.decode(wl.bf16_to_f64(inp.q[seqs]), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
-                           inp.block_table.numpy()[seqs], inp.seq_lens.numpy()[seqs], scale)
+                           inp.block_table.numpy()[seqs], inp.seq_lens.numpy()[seqs], scale,
+                           page_size=inp.k_pool.shape[2])
     return o, lse
 
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("use_ws", [False, True])
-@pytest.mark.parametrize("lens", [(1, 40), (1, 1100)])
-def test_decode_small_elementwise(d, use_ws, lens):
-    say(f"decode d={d} ws={use_ws} lens={lens}")
-    inp = wl.paged_inputs(n_seq=6, H=4, d=d, l_min=lens[0], l_max=lens[1], seed=21 + d + lens[1], spare=5)
+@pytest.mark.parametrize("lens", [(1, 40), (1, 1100), (1000, 5000)])
+@pytest.mark.parametrize("page", [16, 64])
+def test_decode_small_elementwise(d, use_ws, lens, page):
+    say(f"decode d={d} ws={use_ws} lens={lens} page={page}")
+    inp = wl.paged_inputs(n_seq=6, H=4, d=d, l_min=lens[0], l_max=lens[1], seed=21 + d + lens[1], spare=5,
+                          page_size=page)
     scale = 1.0 / math.sqrt(d)
     o, lse = _decode(inp, scale, use_ws)
     ref, ref_lse = _oracle_decode(inp, scale)
@@ -56,24 +59,28 @@ def test_decode_exact_page_multiples_and_single_token():
     v_first = torch.stack([inp.v_pool[int(inp.block_table[s, 0]), :, 0, :] for s in range(4)])
     assert torch.equal(o.cpu().view(torch.int16), v_first.view(torch.int16))
     for L in (16, 32, 512, 528):
-        inp = wl.paged_inputs(n_seq=3, H=2, d=128, l_min=L, l_max=L, seed=L, spare=1)
-        o, _ = _decode(inp, 0.1, True)
-        ref, _ = _oracle_decode(inp, 0.1)
-        check_close(to_np(o), ref, True, what=f"L={L}")
+        for page in (16, 64):
+            inp = wl.paged_inputs(n_seq=3, H=2, d=128, l_min=L, l_max=L, seed=L, spare=1, page_size=page)
+            o, _ = _decode(inp, 0.1, True)
+            ref, _ = _oracle_decode(inp, 0.1)
+            check_close(to_np(o), ref, True, what=f"L={L} page={page}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_gather_bit_exact_small(d):
-    inp = wl.paged_inputs(n_seq=5, H=3, d=d, l_min=1, l_max=90, seed=3 + d, spare=4)
+@pytest.mark.parametrize("page", [16, 64])
+def test_gather_bit_exact_small(d, page):
+    inp = wl.paged_inputs(n_seq=5, H=3, d=d, l_min=1, l_max=290, seed=3 + d, spare=4, page_size=page)
     S, H = 5, 3
     mp = inp.block_table.shape[1]
     sentinel = -12345
-    ko = torch.full((S, H, mp * 16, d), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    vo = torch.full((S, H, mp * 16, d), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ko = torch.full((S, H, mp * page, d), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vo = torch.full((S, H, mp * page, d), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
     A.attn_gather_paged(cuda(inp.k_pool), cuda(inp.v_pool), cuda(inp.block_table), cuda(inp.seq_lens), ko, vo)
     torch.cuda.synchronize()
-    kg = oracle.gather(inp.k_pool.view(torch.int16).numpy(), inp.block_table.numpy(), inp.seq_lens.numpy())
-    vg = oracle.gather(inp.v_pool.view(torch.int16).numpy(), inp.block_table.numpy(), inp.seq_lens.numpy())
+    kg = oracle.gather(inp.k_pool.view(torch.int16).numpy(), inp.block_table.numpy(), inp.seq_lens.numpy(),
+                       page_size=page)
+    vg = oracle.gather(inp.v_pool.view(torch.int16).numpy(), inp.block_table.numpy(), inp.seq_lens.numpy(),
+                       page_size=page)
     kc, vc = ko.view(torch.int16).cpu().numpy(), vo.view(torch.int16).cpu().numpy()
     for s in range(S):
         L = int(inp.seq_lens[s])
@@ -81,9 +88,11 @@ def test_gather_bit_exact_small(d):
         assert np.all(kc[s, :, L:] == sentinel) and np.all(vc[s, :, L:] == sentinel)
 
 
-def test_workload_4_full_size():
-    w = wl.WORKLOADS[4]
-    seed = wl.default_seed(4)
+@pytest.mark.parametrize("key", [4, 15])
+def test_workload_4_full_size(key):
+    """The decode workload at full size (16-token pages; workload 15: 64-token pages)."""
+    w = wl.WORKLOADS[key]
+    seed = wl.default_seed(key)
     say(f"{w.name}: generating pool (seed {seed})")
     inp = wl.paged_inputs(w.n_seq, w.H, w.d, w.l_min, w.l_max, seed=seed, page_size=w.page_size,
                           spare=w.spare_pages)
@@ -101,7 +110,7 @@ def test_workload_4_full_size():
     # bit-exact gather of every sequence against the oracle's gather
     say(f"{w.name}: gather")
     mp = inp.block_table.shape[1]
-    ko = torch.empty((w.n_seq, w.H, mp * 16, w.d), dtype=torch.bfloat16, device="cuda")
+    ko = torch.empty((w.n_seq, w.H, mp * w.page_size, w.d), dtype=torch.bfloat16, device="cuda")
     vo = torch.empty_like(ko)
     A.attn_gather_paged(cuda(inp.k_pool), cuda(inp.v_pool), cuda(inp.block_table), cuda(inp.seq_lens), ko, vo)
     torch.cuda.synchronize()
@@ -110,7 +119,37 @@ def test_workload_4_full_size():
     bt, lens = inp.block_table.numpy(), inp.seq_lens.numpy()
     for s in range(w.n_seq):
         L = int(lens[s])
-        kg = oracle.gather(kpool, bt[s:s + 1], lens[s:s + 1])[0]
-        vg = oracle.gather(vpool, bt[s:s + 1], lens[s:s + 1])[0]
+        kg = oracle.gather(kpool, bt[s:s + 1], lens[s:s + 1], page_size=w.page_size)[0]
+        vg = oracle.gather(vpool, bt[s:s + 1], lens[s:s + 1], page_size=w.page_size)[0]
         assert np.array_equal(ko[s, :, :L].view(torch.int16).cpu().numpy(), kg), s
         assert np.array_equal(vo[s, :, :L].view(torch.int16).cpu().numpy(), vg), s
+
+
+@pytest.mark.parametrize("page", [16, 64])
+def test_out_of_contract_table_and_lengths_stay_in_bounds(page):
+    """Page ids outside [0, num_pages) and lengths outside [0, max_pages *
+    page] break the caller's contract; the kernels clamp both, so the calls
+    complete (results unspecified) and entries of a valid sequence still give
+    its exact result."""
+    S, H, d = 4, 2, 128
+    inp = wl.paged_inputs(S, H, d, 50, 700, seed=71, spare=3, page_size=page, q_rows=40)
+    bt, lens = inp.block_table.clone(), inp.seq_lens.clone()
+    num_pages, mp = inp.k_pool.shape[0], bt.shape[1]
+    bt[1, 0] = -1                          # sequence 1: an id below the pool
+    bt[2, :] = num_pages + 7               # sequence 2: every id past the pool
+    lens[2] = mp * page + 100              # ... and a length past its table row
+    lens[3] = -3                           # sequence 3: a negative length
+    kp, vp, btd, lensd = cuda(inp.k_pool), cuda(inp.v_pool), cuda(bt), cuda(lens)
+    q_dec = cuda(inp.q[:, :, -1].contiguous())
+    o_dec = torch.zeros((S, H, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(A.attn_decode_paged_workspace_size(S, H, d, mp, page), dtype=torch.uint8, device="cuda")
+    A.attn_decode_paged(q_dec, kp, vp, btd, lensd, o_dec, 0.1, workspace=ws)
+    A.attn_decode_paged(q_dec, kp, vp, btd, lensd, torch.zeros_like(o_dec), 0.1)
+    ko = torch.zeros((S, H, mp * page, d), dtype=torch.bfloat16, device="cuda")
+    A.attn_gather_paged(kp, vp, btd, lensd, ko, torch.zeros_like(ko))
+    o_pre = torch.zeros((S, H, 40, d), dtype=torch.bfloat16, device="cuda")
+    A.attn_prefill_paged(cuda(inp.q), kp, vp, btd, lensd, o_pre, 0.1)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode(wl.bf16_to_f64(inp.q[:1, :, -1]), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
+                           inp.block_table.numpy()[:1], inp.seq_lens.numpy()[:1], 0.1, page_size=page)
+    check_close(to_np(o_dec[:1]), ref, True, what="valid sequence beside broken ones")

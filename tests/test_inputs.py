@@ -43,7 +43,7 @@ def test_paged_inputs_deterministic():
 
 
 def test_workload_table():
-    assert set(wl.WORKLOADS) == set(range(1, 15))
+    assert set(wl.WORKLOADS) == set(range(1, 16))
     assert wl.WORKLOADS[14].page_size == 16 and wl.WORKLOADS[11].page_size == 64
     w = wl.WORKLOADS[3]
     assert (w.B, w.H, w.N, w.d, w.mask, w.window) == (2, 32, 8192, 128, "sliding", 4096)

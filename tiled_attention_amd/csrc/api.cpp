@@ -162,8 +162,8 @@ attn_status attn_quant_fp8_block_pow2(const float* x, uint8_t* codes, float* sca
 }
 
 size_t attn_decode_paged_workspace_size(int S, int H, int d, int max_pages, int page_size) {
-  if (S < 1 || H < 1 || max_pages < 1 || (d != 64 && d != 128) || page_size != 16) return 0;
-  return attn::decode_workspace_bytes(S, H, d, max_pages);
+  if (S < 1 || H < 1 || max_pages < 1 || (d != 64 && d != 128) || (page_size != 16 && page_size != 64)) return 0;
+  return attn::decode_workspace_bytes(S, H, d, max_pages, page_size);
 }
 
 static attn_status check_paged(const void* k_pool, const void* v_pool, const int32_t* block_table,
@@ -176,7 +176,7 @@ static attn_status check_paged(const void* k_pool, const void* v_pool, const int
   if ((long long)S * max_pages >= (1LL << 31) || (long long)num_pages * H * page_size >= (1LL << 31))
     return ATTN_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if (page_size != 16) return ATTN_ERR_UNSUPPORTED;
+  if (page_size != 16 && page_size != 64) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -192,7 +192,7 @@ attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_p
   if (st != ATTN_OK) return st;
   if (workspace) {
     if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
-    if (workspace_bytes < attn::decode_workspace_bytes(S, H, d, max_pages)) return ATTN_ERR_WORKSPACE;
+    if (workspace_bytes < attn::decode_workspace_bytes(S, H, d, max_pages, page_size)) return ATTN_ERR_WORKSPACE;
   }
   attn::DecodeArgs a{};
   a.q = q;
@@ -207,6 +207,8 @@ attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_p
   a.H = H;
   a.d = d;
   a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
   a.scale = scale;
   return launched(attn::launch_decode(a, (hipStream_t)stream));
 }
@@ -277,9 +279,7 @@ attn_status attn_gather_paged(const void* k_pool, const void* v_pool, const int3
   if (!k_out || !v_out) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(k_out) || !aligned16(v_out)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_INVALID_ARG;
-  // the copy takes the decode's 16-token pages and the prefill's 64-token pages
-  attn_status st = check_paged(k_pool, v_pool, block_table, seq_lens, S, H, d, page_size == 64 ? 16 : page_size,
-                               max_pages, num_pages);
+  attn_status st = check_paged(k_pool, v_pool, block_table, seq_lens, S, H, d, page_size, max_pages, num_pages);
   if (st != ATTN_OK) return st;
   if ((long long)S * H * max_pages * page_size >= (1LL << 31)) return ATTN_ERR_INVALID_ARG;
   attn::GatherArgs a{};
@@ -293,6 +293,7 @@ attn_status attn_gather_paged(const void* k_pool, const void* v_pool, const int3
   a.H = H;
   a.d = d;
   a.max_pages = max_pages;
+  a.num_pages = num_pages;
   a.elem_bytes = dtype == ATTN_F32 ? 4 : 2;
   a.page_size = page_size;
   return launched(attn::launch_gather(a, (hipStream_t)stream));

@@ -47,7 +47,7 @@ struct DecodeArgs {
   void* o;
   float* lse;
   void* workspace;      // nullable
-  int S, H, d, max_pages;
+  int S, H, d, max_pages, num_pages, page_size;   // page_size 16 or 64
   float scale;
 };
 
@@ -58,12 +58,13 @@ struct GatherArgs {
   const int32_t* seq_lens;
   void* k_out;
   void* v_out;
-  int S, H, d, max_pages, elem_bytes, page_size;
+  int S, H, d, max_pages, num_pages, elem_bytes, page_size;
 };
 
-// Pages per split of the split-KV decode, and the resulting workspace size.
+// 16-token units per split of the split-KV decode, and the resulting
+// workspace size for block-table rows of max_pages pages of page_size tokens.
 constexpr int kDecodeSplitPages = 64;
-size_t decode_workspace_bytes(int S, int H, int d, int max_pages);
+size_t decode_workspace_bytes(int S, int H, int d, int max_pages, int page_size);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

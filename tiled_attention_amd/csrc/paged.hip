@@ -1,8 +1,10 @@
 // Paged-KV decode and page gather on gfx950.
 //
-// Pool layout [num_pages, H, 16, d] bf16 with a per-sequence block table
-// ("Optimizing Triton kernels for custom attention patterns on H100",
-// Pattern C, gather_pages). Decode is bound by HBM bandwidth: every cached
+// Pool layout [num_pages, H, page, d] bf16 (page = 16 or 64 tokens) with a
+// per-sequence block table ("Optimizing Triton kernels for custom attention
+// patterns on H100", Pattern C, gather_pages). The decode walks 16-token
+// units: a 64-token page is four of them, contiguous in its (page, head)
+// slice. Decode is bound by HBM bandwidth: every cached
 // K/V byte is read once, so the kernels are built around keeping enough bytes
 // in flight, not around the matrix cores.
 //
@@ -39,7 +41,8 @@ struct DecParams {
   float* lse;
   float* ws_acc;   // [S, H, max_splits, d]
   float* ws_ml;    // [S, H, max_splits, 2]
-  int H, max_pages, split_pages, max_splits, direct;
+  int H, max_pages, split_pages, max_splits, direct;   // max_pages: block-table row length
+  int num_pages, len_max;   // page ids are clamped into [0, num_pages), lengths into [0, len_max]
   float scale_log2;
 };
 
@@ -69,11 +72,13 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 // past 2^16 trigger a rebase; below it P stays far inside fp32.
 constexpr float kDecodeHeadroom = 16.f;
 
-template <int D>
+// SUB = 16-token units per page (1 or 4); "page" below means such a unit.
+template <int D, int SUB>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
-  // A (page, head) slice is 16 keys x D bf16, contiguous. Load j of a lane
+  // A unit of one head is 16 keys x D bf16, contiguous. Load j of a lane
   // reads 16 bytes at 1024 j + 16 lane: key j*KPJ + lane/LPK, dims
   // 8 (lane % LPK) .. +7. Every load instruction reads 1 KB contiguously.
+  static_assert(SUB == 1 || SUB == 4, "16- or 64-token pages");
   constexpr int SLICE = PAGE * D * 2;
   constexpr int NJ = SLICE / 1024;   // loads per lane per page and tensor
   constexpr int LPK = D / 8;         // lanes per key
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
   const int s = blockIdx.z;
   const int lane = threadIdx.x;
   const int H = p.H;
-  const int len = p.lens[s];
+  const int len = min(max(p.lens[s], 0), p.len_max);
   const int npages = (len + PAGE - 1) / PAGE;
   const int pg0 = split * p.split_pages;
   if (pg0 >= npages) return;
@@ -105,31 +110,34 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
   float m_ref = -INFINITY, l_lane = 0.f;
   const float c = p.scale_log2;
   const int32_t* bt = p.bt + (size_t)s * p.max_pages;
-  const char* kbase = (const char*)p.kp + (size_t)h * SLICE + 16 * lane;
-  const char* vbase = (const char*)p.vp + (size_t)h * SLICE + 16 * lane;
-  const size_t page_stride = (size_t)H * SLICE;
+  const char* kbase = (const char*)p.kp + (size_t)h * SUB * SLICE + 16 * lane;
+  const char* vbase = (const char*)p.vp + (size_t)h * SUB * SLICE + 16 * lane;
+  const size_t page_stride = (size_t)H * SUB * SLICE;
 
   int pid_vec = 0, batch = pg0 - 64;
   for (int pg = pg0; pg < pg1; pg += 2) {
     if (pg - batch == 64) {
-      // the next 64 page ids of the range, one per lane
+      // the page ids of the next 64 units of the range, one per lane (SUB
+      // consecutive units share a page)
       batch = pg;
-      pid_vec = pg + lane < pg1 ? bt[pg + lane] : 0;
+      pid_vec = pg + lane < pg1 ? min(max(bt[(pg + lane) / SUB], 0), p.num_pages - 1) : 0;
     }
     const int pid0 = __builtin_amdgcn_readlane(pid_vec, pg - batch);
     const bool two = pg + 1 < pg1;
-    // a missing second page reads the first again (its P is 0)
+    // a missing second unit reads the first again (its P is 0)
     const int pid1 = two ? __builtin_amdgcn_readlane(pid_vec, pg + 1 - batch) : pid0;
+    const size_t off0 = pid0 * page_stride + (size_t)(pg % SUB) * SLICE;
+    const size_t off1 = two ? pid1 * page_stride + (size_t)((pg + 1) % SUB) * SLICE : off0;
     u32x4 kr[2][NJ], vr[2][NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      kr[0][j] = __builtin_nontemporal_load((const u32x4*)(kbase + pid0 * page_stride + 1024 * j));
-      kr[1][j] = __builtin_nontemporal_load((const u32x4*)(kbase + pid1 * page_stride + 1024 * j));
+      kr[0][j] = __builtin_nontemporal_load((const u32x4*)(kbase + off0 + 1024 * j));
+      kr[1][j] = __builtin_nontemporal_load((const u32x4*)(kbase + off1 + 1024 * j));
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      vr[0][j] = __builtin_nontemporal_load((const u32x4*)(vbase + pid0 * page_stride + 1024 * j));
-      vr[1][j] = __builtin_nontemporal_load((const u32x4*)(vbase + pid1 * page_stride + 1024 * j));
+      vr[0][j] = __builtin_nontemporal_load((const u32x4*)(vbase + off0 + 1024 * j));
+      vr[1][j] = __builtin_nontemporal_load((const u32x4*)(vbase + off1 + 1024 * j));
     }
     // scores (log2 units) of the lane's keys; -inf past the sequence or the range
     float sc[2][NJ];
@@ -225,7 +233,7 @@ template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecParams p) {
   const int sh = blockIdx.x;
   const int s = sh / p.H;
-  const int len = p.lens[s];
+  const int len = min(max(p.lens[s], 0), p.len_max);
   const int npages = (len + PAGE - 1) / PAGE;
   const int nsplit = (npages + p.split_pages - 1) / p.split_pages;
   const size_t base = (size_t)sh * p.max_splits;
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   const int len = a.seq_lens[s];
   if (slot * page >= len) return;
   const int rows = min(page, len - slot * page);
-  const int pid = a.block_table[(size_t)s * a.max_pages + slot];
+  const int pid = min(max(a.block_table[(size_t)s * a.max_pages + slot], 0), a.num_pages - 1);
   const int row_chunks = a.d * a.elem_bytes / 16;
   const int per_head = rows * row_chunks;
   const int total = a.H * per_head;
@@ -271,8 +279,9 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 
 int split_count(int max_pages) { return (max_pages + kDecodeSplitPages - 1) / kDecodeSplitPages; }
 
-template <int D>
+template <int D, int SUB>
 hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
+  const int units = a.max_pages * SUB;   // 16-token units a table row can address
   DecParams p;
   p.q = (const __bf16*)a.q;
   p.kp = (const __bf16*)a.k_pool;
@@ -283,26 +292,28 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
   p.lse = a.lse;
   p.H = a.H;
   p.max_pages = a.max_pages;
+  p.num_pages = a.num_pages;
+  p.len_max = a.max_pages * SUB * PAGE;
   p.scale_log2 = a.scale * kLog2e;
   if (a.workspace == nullptr) {
     p.direct = 1;
-    p.split_pages = a.max_pages;
+    p.split_pages = units;
     p.max_splits = 1;
     p.ws_acc = nullptr;
     p.ws_ml = nullptr;
-    hipLaunchKernelGGL(decode_split_kernel<D>, dim3(a.H, 1, a.S), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, SUB>), dim3(a.H, 1, a.S), dim3(64), 0, stream, p);
     return hipGetLastError();
   }
   p.direct = 0;
   p.split_pages = kDecodeSplitPages;
-  p.max_splits = split_count(a.max_pages);
+  p.max_splits = split_count(units);
   p.ws_acc = (float*)a.workspace;
   p.ws_ml = p.ws_acc + (size_t)a.S * a.H * p.max_splits * D;
   // heads innermost: the waves of one (sequence, range) run together, and the
   // slices they read of each page -- one per head -- are adjacent in the pool,
   // so the page's H * 4 KB are fetched as one contiguous run (measured 14%
   // faster than ranges innermost, whose concurrent reads are scattered 4 KB)
-  hipLaunchKernelGGL(decode_split_kernel<D>, dim3(a.H, p.max_splits, a.S), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, SUB>), dim3(a.H, p.max_splits, a.S), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.S * a.H), dim3(D), 0, stream, p);
@@ -311,13 +322,14 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t decode_workspace_bytes(int S, int H, int d, int max_pages) {
-  const size_t slots = (size_t)S * H * split_count(max_pages);
+size_t decode_workspace_bytes(int S, int H, int d, int max_pages, int page_size) {
+  const size_t slots = (size_t)S * H * split_count(max_pages * (page_size / PAGE));
   return slots * ((size_t)d + 2) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  return a.d == 64 ? launch_decode_d<64>(a, stream) : launch_decode_d<128>(a, stream);
+  if (a.page_size == 64) return a.d == 64 ? launch_decode_d<64, 4>(a, stream) : launch_decode_d<128, 4>(a, stream);
+  return a.d == 64 ? launch_decode_d<64, 1>(a, stream) : launch_decode_d<128, 1>(a, stream);
 }
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {

@@ -112,6 +112,9 @@ WORKLOADS = {
     # the paged prefill of workload 11 over the decode's 16-token pages
     14: Workload(14, "paged_prefill_bf16_s16_h32_d128_p16_q512_l1024to8192", "paged_prefill", H=32, d=128,
                  n_seq=16, l_min=1024, l_max=8192, page_size=16, q_len=512),
+    # the decode of workload 4 over 64-token pages
+    15: Workload(15, "paged_decode_bf16_s64_h32_d128_p64_l512to8192", "paged", H=32, d=128,
+                 n_seq=64, l_min=512, l_max=8192, page_size=64),
 }
 
 
