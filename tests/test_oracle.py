@@ -220,19 +220,20 @@ def test_split_and_merge_matches_two_pass(mask, window):
 
 # ----------------------------------------------------------------- paged
 
-def test_paged_gather_round_trip_and_decode():
+@pytest.mark.parametrize("page", [16, 64])
+def test_paged_gather_round_trip_and_decode(page):
     from tiled_attention_amd.workloads import paged_inputs, bf16_to_f64
-    inp = paged_inputs(n_seq=5, H=3, d=8, l_min=1, l_max=70, seed=3, spare=4, keep_dense=True)
+    inp = paged_inputs(n_seq=5, H=3, d=8, l_min=1, l_max=170, seed=3, spare=4, keep_dense=True, page_size=page)
     pool_bits = inp.k_pool.view(torch.int16).numpy()
-    got = oracle.gather(pool_bits, inp.block_table.numpy(), inp.seq_lens.numpy())
+    got = oracle.gather(pool_bits, inp.block_table.numpy(), inp.seq_lens.numpy(), page_size=page)
     for s in range(5):
         want = inp.k_dense[s].view(torch.int16).numpy()
         assert np.array_equal(got[s], want)           # bit-identical copy
-    vals = oracle.gather(inp.v_pool.float().numpy(), inp.block_table.numpy(), inp.seq_lens.numpy())
+    vals = oracle.gather(inp.v_pool.float().numpy(), inp.block_table.numpy(), inp.seq_lens.numpy(), page_size=page)
     assert not any(np.isnan(x).any() for x in vals)  # poison never read
     scale = 1.0 / math.sqrt(8)
     o, lse = oracle.decode(bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
-                           inp.block_table.numpy(), inp.seq_lens.numpy(), scale)
+                           inp.block_table.numpy(), inp.seq_lens.numpy(), scale, page_size=page)
     for s in range(5):
         L = int(inp.seq_lens[s])
         kd, vd = bf16_to_f64(inp.k_dense[s]), bf16_to_f64(inp.v_dense[s])
