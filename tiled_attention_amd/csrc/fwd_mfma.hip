@@ -1,5 +1,5 @@
 // Flash-attention forward on gfx950 MFMA: bf16 Q/K/V, or fp8 (E4M3FN) Q/K with
-// per-128-row-block scales and bf16 V.
+// per-128-row-block scales and bf16 or fp8 V; K/V dense or in a paged pool.
 //
 // Method: "Flash MSA Attention Kernel Implementation Tutorial", "Understanding
 // Flash MSA Core Mechanics" -- a Q tile stays on chip while K/V tiles stream
