@@ -174,7 +174,8 @@ enum UnitOrder {
   ORDER_TILES = 3    // one Q tile per unit, tile-major from the last tile down (costs never fall with
                      // the tile index for these masks), heads innermost so a head stays on one XCD
 };
-constexpr int kOrderMaxDocs = 8192;  // document offsets staged in LDS for the costing
+constexpr int kOrderMaxDocs = 8192;  // document offsets staged in LDS for the costing (and the LDS
+                                     // must hold them behind the 2 NT ints of costs and ranks)
 
 __device__ __forceinline__ float half_swap_max(float x) {
   // max over lane l and lane l^32
@@ -286,7 +287,10 @@ struct QTile {
   bf16x8 P[2][4];           // P of two tiles: [buffer][k-step]
   i32x8 P8[2];              // fp8 V: P of two tiles as fp8 bytes, byte k = key 32 hl + k
 
-  __device__ __forceinline__ QTile(const Params& p_, unsigned char* smem_, int bh_, int qt) : p(p_), smem(smem_) {
+  // offs: the document offsets (p.doc, or a copy of them in LDS that the
+  // ring does not overwrite before the workgroup's next barrier)
+  __device__ __forceinline__ QTile(const Params& p_, unsigned char* smem_, int bh_, int qt, const int32_t* offs)
+      : p(p_), smem(smem_) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave logic scalar
@@ -333,7 +337,16 @@ struct QTile {
       k_next = 0;
       v_next = 0;
     } else {
-      sp = row_spans(p.mask, p.window, p.doc, p.nd, N, m0, m1 - 1, wr0, wr1, qsrc);
+      sp = row_spans(p.mask, p.window, offs, p.nd, N, m0, m1 - 1, wr0, wr1, qsrc);
+      // the tile's and the wave's spans are uniform; offsets read through a
+      // pointer that may be in LDS come back in VGPRs, so say so
+      auto uniform = [](KeySpan k) {
+        return KeySpan{__builtin_amdgcn_readfirstlane(k.lo), __builtin_amdgcn_readfirstlane(k.hi)};
+      };
+      sp.tile_first = uniform(sp.tile_first);
+      sp.tile_last = uniform(sp.tile_last);
+      sp.wave_first = uniform(sp.wave_first);
+      sp.wave_last = uniform(sp.wave_last);
       touched_tiles(sp.tile_first, sp.tile_last, BN, &t_lo, &NK);
       NK -= t_lo;
     }
@@ -925,22 +938,38 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
     } else {
       c = min(max(p.pg_lens[tid], 0), p.pg_max * p.pg_page);
     }
-    cost[tid] = c;
+    // one key per group orders by cost, then by index: (cost + 1) * 256 +
+    // (255 - group); keys are distinct, costs stay below 2^23
+    cost[tid] = (c + 1) * 256 + (255 - tid);
+  } else if (tid < ((G + 15) & ~15)) {
+    cost[tid] = 0;                         // padding to whole 64-byte rounds; below every key
   }
   __syncthreads();
   if (tid < G) {
-    const int c = cost[tid];
+    // rank = number of larger keys. The keys are read sixteen at a time
+    // (four broadcast 16-byte LDS reads in flight per round): one read per
+    // group in turn took about 8000 cycles at 128 groups, and every
+    // workgroup ranks all groups.
+    const unsigned key = (unsigned)cost[tid];
     int r = 0;
-    for (int g = 0; g < G; ++g) {
-      const int cg = cost[g];
-      r += (cg > c || (cg == c && g < tid)) ? 1 : 0;
+    const i32x4* c4 = (const i32x4*)cost;
+    const int n4 = ((G + 15) & ~15) >> 2;  // 16-byte reads covering the padded keys, a multiple of 4
+    for (int g4 = 0; g4 < n4; g4 += 4) {
+      const i32x4 v0 = c4[g4], v1 = c4[g4 + 1], v2 = c4[g4 + 2], v3 = c4[g4 + 3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        r += ((unsigned)v0[e] > key) + ((unsigned)v1[e] > key) + ((unsigned)v2[e] > key) + ((unsigned)v3[e] > key);
     }
     order[r] = tid;
   }
   __syncthreads();
-  const int grp = order[u / p.per_group];
+  // the ranks are a permutation of [0, G); the clamp keeps a mistake in them
+  // from turning into a tile index outside the tensors
+  const int grp = min(max(order[u / p.per_group], 0), G - 1);
   const int sub = u - (u / p.per_group) * p.per_group;
-  __syncthreads();  // the LDS is the ring's from here on
+  // no barrier here: nothing writes these arrays before the caller's next
+  // barrier (the page-id staging, or the one after the document spans), and
+  // the ring's DMA starts only after it
   if (p.order == ORDER_DOC) {             // group = Q tile, sub = head
     *bh = sub;
     *w = p.n_qtiles - 1 - grp;
@@ -979,14 +1008,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // so the two latencies overlap
   const int ta = w, tb = p.n_qtiles - 1 - w;
   {
-    QTile<D, FP8, OUT_F32, PG, V8> a(p, smem, bh, tb);
+    // with the ordering's LDS copy of the document offsets, the spans are
+    // searched there (a search in global memory costs several dependent
+    // round trips per workgroup); a barrier then frees the LDS for the ring
+    const bool lds_offs = p.order == ORDER_DOC;
+    QTile<D, FP8, OUT_F32, PG, V8> a(p, smem, bh, tb, lds_offs ? (const int32_t*)(smem + 2 * NT * sizeof(int)) : p.doc);
     a.load_q();
+    if (lds_offs) __syncthreads();
     a.start_stream();
     a.loop();
     a.epilogue();
   }
   if (p.pair && ta != tb) {
-    QTile<D, FP8, OUT_F32, PG, V8> b(p, smem, bh, ta);
+    QTile<D, FP8, OUT_F32, PG, V8> b(p, smem, bh, ta, p.doc);
     b.load_q();
     b.start_stream();
     b.loop();
@@ -1028,7 +1062,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.window = a.window;
   p.nd = a.num_docs;
   if (is_document(a.mask)) {
-    if (p.n_qtiles <= NT && a.num_docs + 1 <= kOrderMaxDocs) {
+    if (p.n_qtiles <= NT && a.num_docs + 1 <= kOrderMaxDocs &&
+        (2 * NT + a.num_docs + 1) * (int)sizeof(int) <= Cfg<D, FP8, V8>::LDS) {
       p.order = ORDER_DOC;
       p.groups = p.n_qtiles;
       p.per_group = a.BH;
