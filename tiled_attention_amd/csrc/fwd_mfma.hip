@@ -941,31 +941,39 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
     // one key per group orders by cost, then by index: (cost + 1) * 256 +
     // (255 - group); keys are distinct, costs stay below 2^23
     cost[tid] = (c + 1) * 256 + (255 - tid);
+    order[tid] = 0;                        // rank counter of group tid
   } else if (tid < ((G + 15) & ~15)) {
     cost[tid] = 0;                         // padding to whole 64-byte rounds; below every key
   }
   __syncthreads();
-  if (tid < G) {
-    // rank = number of larger keys. The keys are read sixteen at a time
-    // (four broadcast 16-byte LDS reads in flight per round): one read per
-    // group in turn took about 8000 cycles at 128 groups, and every
-    // workgroup ranks all groups.
-    const unsigned key = (unsigned)cost[tid];
+  // rank = number of larger keys. The keys are read sixteen at a time (four
+  // broadcast 16-byte LDS reads in flight per round), and with G <= 128
+  // groups two or four threads share a group's rounds and add their counts:
+  // one read per group in turn took about 8000 cycles at 128 groups, and
+  // every workgroup ranks all groups.
+  const int parts = G <= NT / 4 ? 4 : G <= NT / 2 ? 2 : 1;
+  if (tid < parts * G) {
+    const int part = (tid >= G) + (tid >= 2 * G) + (tid >= 3 * G);
+    const int g = tid - part * G;
+    const unsigned key = (unsigned)cost[g];
     int r = 0;
     const i32x4* c4 = (const i32x4*)cost;
-    const int n4 = ((G + 15) & ~15) >> 2;  // 16-byte reads covering the padded keys, a multiple of 4
-    for (int g4 = 0; g4 < n4; g4 += 4) {
-      const i32x4 v0 = c4[g4], v1 = c4[g4 + 1], v2 = c4[g4 + 2], v3 = c4[g4 + 3];
+    const int n16 = (G + 15) >> 4;         // rounds of sixteen keys over the padded keys
+    for (int round = part; round < n16; round += parts) {
+      const i32x4 v0 = c4[4 * round], v1 = c4[4 * round + 1], v2 = c4[4 * round + 2], v3 = c4[4 * round + 3];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         r += ((unsigned)v0[e] > key) + ((unsigned)v1[e] > key) + ((unsigned)v2[e] > key) + ((unsigned)v3[e] > key);
     }
-    order[r] = tid;
+    atomicAdd(&order[g], r);
   }
   __syncthreads();
-  // the ranks are a permutation of [0, G); the clamp keeps a mistake in them
-  // from turning into a tile index outside the tensors
-  const int grp = min(max(order[u / p.per_group], 0), G - 1);
+  // the ranks are a permutation of [0, G); the clamps keep a mistake in them
+  // from turning into an access outside the table or a tile index outside
+  // the tensors. The keys are dead: their array takes the group of each rank.
+  if (tid < G) cost[min(max(order[tid], 0), G - 1)] = tid;
+  __syncthreads();
+  const int grp = min(max(cost[u / p.per_group], 0), G - 1);
   const int sub = u - (u / p.per_group) * p.per_group;
   // no barrier here: nothing writes these arrays before the caller's next
   // barrier (the page-id staging, or the one after the document spans), and
