@@ -94,3 +94,20 @@ def test_fp8_full_workload_sampled():
     rr0 = rel_rmse(np.concatenate(got), np.concatenate(orig))
     say(f"{w.name}: rel RMSE {rr:.3g} vs dequantised oracle, {rr0:.3g} vs the fp32-input oracle (reported)")
     assert rr <= min(FP8_REL_RMSE, P_ROUNDING_RMSE)
+
+
+def test_fp8_full_d64_many_documents():
+    """All-fp8 at d = 64 has the smallest LDS ring (32 KB); 8000 one-token
+    documents do not fit behind the heaviest-first ordering's arrays there,
+    so the launch keeps the natural order and searches the offsets in global
+    memory. Every row sees only its own key: O is that row of the
+    dequantised V (P = 1 exactly) and LSE is the scaled self-score."""
+    B, H, N, d = 1, 1, 8000, 64
+    offs = np.arange(N + 1)
+    o, lse, (qh, kh, vh), _ = _full(B, H, N, d, "document", 0, seed=77, offs=offs)
+    assert np.max(np.abs(to_np(o)[0, 0] - vh[0, 0])) <= 2 ** -8 * np.max(np.abs(vh[0, 0])) + 1e-6
+    rows = sample_rows(N, 77)
+    ref, ref_lse = oracle.attention(qh[0, 0], kh[0, 0], vh[0, 0], 1.0 / math.sqrt(d), "document", rows=rows,
+                                    doc_offsets=offs)
+    assert rel_rmse(to_np(o)[0, 0][rows], ref) <= P_ROUNDING_RMSE
+    check_lse_fp8(to_np(lse)[0, 0][rows], ref_lse)
