@@ -282,10 +282,20 @@ class PagedCross:
                 "seed": self.seed}
 
 
-def event_time_ms(step, reps, warmup=3):
-    """Average duration of one step from HIP events on the launch stream."""
+def event_time_ms(step, reps, warmup=3, settle_ms=30.0):
+    """Average duration of one step from HIP events on the launch stream,
+    after `warmup` calls and then enough further calls to keep the GPU busy
+    for about settle_ms (at most 300): a workload's first launches run slower
+    (clock ramp, first touches of its buffers)."""
     import torch
     for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    one_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(min(300, int(settle_ms / max(one_ms, 1e-3)))):
         step()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
