@@ -65,6 +65,25 @@ def test_fwd_f32_elementwise(case):
     assert np.max(np.abs(to_np(lse) - ref_lse)) <= 1e-4
 
 
+@pytest.mark.parametrize("case", [(2, 8, 4096, 64, "causal"), (1, 16, 2100, 128, "none")],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_fwd_f32_large_grid_sampled(case):
+    """Grids of at least one 128-row workgroup per CU take the 128-row fp32
+    layout (smaller ones split the key tiles over the waves of 32-row
+    workgroups); sampled rows of two heads against the oracle."""
+    B, H, N, d, mask = case
+    say(f"fwd f32 large grid {case}")
+    q, k, v = (torch.from_numpy(x) for x in wl.dense_inputs(B, H, N, d, seed=13 + N))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run(q, k, v, scale, mask, 0, torch.float32)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        rows = sample_rows(N, 13 + h)
+        ref, ref_lse = oracle.attention(q[b, h].numpy(), k[b, h].numpy(), v[b, h].numpy(), scale, mask, rows=rows)
+        err = check_close(to_np(o[b, h][rows]), ref, False, what=f"{case} {(b, h)}")
+        assert err <= 1e-4, err
+        assert np.max(np.abs(to_np(lse[b, h][rows]) - ref_lse)) <= 1e-4
+
+
 def test_fwd_f32_workload_1_full():
     w = wl.WORKLOADS[1]
     q, k, v = (torch.from_numpy(x) for x in wl.dense_inputs(w.B, w.H, w.N, w.d, seed=wl.default_seed(1)))

@@ -22,6 +22,8 @@ namespace {
 constexpr int BMF = 128;
 constexpr int BNF = 32;
 constexpr int NTF = 256;
+// below this many 128-row workgroups (one per CU) the split-key layout runs instead
+constexpr int kSmallGridWorkgroups = 256;
 
 struct ParamsF {
   const float* q;
@@ -142,6 +144,159 @@ __global__ __launch_bounds__(NTF) void fwd_f32_kernel(ParamsF p) {
   }
 }
 
+// Small grids (fewer workgroups of 128 rows than CUs): a workgroup owns 32
+// query rows and its four waves split the key tiles among themselves (tile
+// t_lo + j goes to wave j % 4), each wave staging its tiles in its own LDS
+// region, so the waves need no workgroup barrier in the loop. The four
+// partial states (m, l, acc) per row are merged at the end with the same
+// rescale algebra as the split-KV decode. A lane does a quarter of the key
+// work of the 128-row layout, so such a grid finishes sooner.
+constexpr int BMS = 32;  // query rows per workgroup
+constexpr int NWS = 4;   // waves, each taking every fourth key tile
+
+// orders the LDS writes of a wave's lanes before their reads by other lanes
+// of the same wave (and the reads before the next writes)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(NTF) void fwd_f32_split_kernel(ParamsF p) {
+  constexpr int HALF = D / 2;
+  constexpr int PITCH = D + 4;  // floats; keeps 16-byte row starts off one bank
+  constexpr int TILE = BNF * PITCH;
+  static_assert(64 * (HALF + 2) <= TILE, "a wave's merge record fits its tile region");
+  __shared__ __attribute__((aligned(16))) float ks[NWS * TILE];
+  __shared__ __attribute__((aligned(16))) float vs[NWS * TILE];
+
+  const int bh = blockIdx.y;
+  const int m0 = blockIdx.x * BMS;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int half = lane & 1;
+  const int N = p.N;
+  const int m1 = min(m0 + BMS, N);
+  const int qrow = m0 + (lane >> 1);
+  const size_t head = (size_t)bh * N;
+  const RowSpans sp = row_spans(p.mask, p.window, p.doc, p.nd, N, m0, m1 - 1, m0, m1 - 1, min(qrow, N - 1));
+
+  float q[HALF];
+  float acc[HALF];
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    q[i] = qrow < N ? p.q[(head + qrow) * D + half * HALF + i] : 0.f;
+    acc[i] = 0.f;
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+
+  int t_lo, t_hi;
+  touched_tiles(sp.tile_first, sp.tile_last, BNF, &t_lo, &t_hi);
+  float* kw = ks + wave * TILE;
+  float* vw = vs + wave * TILE;
+  constexpr int CH = D / 4;  // float4 per row
+  const float c = p.scale_log2;
+  for (int kt = t_lo + wave; kt < t_hi; kt += NWS) {
+    const int n0 = kt * BNF;
+#pragma unroll
+    for (int u = 0; u < BNF * CH / 64; ++u) {
+      const int cc = lane + 64 * u;
+      const int r = cc / CH, col = cc % CH;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      if (n0 + r < N) {
+        kv = *(const float4*)(p.k + (head + n0 + r) * D + 4 * col);
+        vv = *(const float4*)(p.v + (head + n0 + r) * D + 4 * col);
+      }
+      *(float4*)(kw + r * PITCH + 4 * col) = kv;
+      *(float4*)(vw + r * PITCH + 4 * col) = vv;
+    }
+    wave_lds_sync();
+    float s[BNF];
+#pragma unroll
+    for (int j = 0; j < BNF; ++j) {
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < HALF; i += 4) {
+        const float4 kk = *(const float4*)(kw + j * PITCH + half * HALF + i);
+        dot = __builtin_fmaf(q[i], kk.x, dot);
+        dot = __builtin_fmaf(q[i + 1], kk.y, dot);
+        dot = __builtin_fmaf(q[i + 2], kk.z, dot);
+        dot = __builtin_fmaf(q[i + 3], kk.w, dot);
+      }
+      dot += __shfl_xor(dot, 1);
+      const int key = n0 + j;
+      s[j] = (key >= sp.lane.lo && key <= sp.lane.hi) ? dot : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int j = 1; j < BNF; ++j) mx = fmaxf(mx, s[j]);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < BNF; ++j) {
+      s[j] = exp2f(__builtin_fmaf(s[j], c, -m_use));
+      psum += s[j];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < BNF; ++j) {
+#pragma unroll
+      for (int i = 0; i < HALF; i += 4) {
+        const float4 vv = *(const float4*)(vw + j * PITCH + half * HALF + i);
+        acc[i] = __builtin_fmaf(s[j], vv.x, acc[i]);
+        acc[i + 1] = __builtin_fmaf(s[j], vv.y, acc[i + 1]);
+        acc[i + 2] = __builtin_fmaf(s[j], vv.z, acc[i + 2]);
+        acc[i + 3] = __builtin_fmaf(s[j], vv.w, acc[i + 3]);
+      }
+    }
+    wave_lds_sync();
+  }
+  // merge: each wave leaves (m, l, acc) per lane in its K region; wave 0
+  // combines m* = max m_w, l* = sum 2^(m_w - m*) l_w, acc* likewise
+  __syncthreads();
+  float* rec = kw + lane * (HALF + 2);
+  rec[0] = m_run;
+  rec[1] = l_run;
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) rec[2 + i] = acc[i];
+  __syncthreads();
+  if (wave != 0 || qrow >= N) return;
+  float m_star = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NWS; ++w) m_star = fmaxf(m_star, ks[w * TILE + lane * (HALF + 2)]);
+  const float m_use = m_star == -INFINITY ? 0.f : m_star;
+  float l_tot = 0.f;
+  float o[HALF];
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) o[i] = 0.f;
+#pragma unroll
+  for (int w = 0; w < NWS; ++w) {
+    const float* r = ks + w * TILE + lane * (HALF + 2);
+    const float wt = exp2f(r[0] - m_use);
+    l_tot += wt * r[1];
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) o[i] += wt * r[2 + i];
+  }
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const float x = o[i] * inv;
+    if constexpr (OUT_F32)
+      ((float*)p.o)[(head + qrow) * D + half * HALF + i] = x;
+    else
+      ((__bf16*)p.o)[(head + qrow) * D + half * HALF + i] = (__bf16)x;
+  }
+  if (p.lse != nullptr && half == 0)
+    p.lse[head + qrow] = l_tot > 0.f ? (m_star + log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
 template <int D, bool OUT_F32>
 hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
   ParamsF p;
@@ -157,6 +312,11 @@ hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
   p.nd = a.num_docs;
   p.n_qtiles = (a.N + BMF - 1) / BMF;
   p.scale_log2 = a.scale * kLog2e;
+  if ((long long)p.n_qtiles * a.BH < kSmallGridWorkgroups) {
+    dim3 grid((a.N + BMS - 1) / BMS, a.BH);
+    hipLaunchKernelGGL((fwd_f32_split_kernel<D, OUT_F32>), grid, dim3(NTF), 0, stream, p);
+    return hipGetLastError();
+  }
   dim3 grid(p.n_qtiles, a.BH);
   hipLaunchKernelGGL((fwd_f32_kernel<D, OUT_F32>), grid, dim3(NTF), 0, stream, p);
   return hipGetLastError();
