@@ -32,7 +32,7 @@ struct ParamsF {
   void* o;
   float* lse;
   const int32_t* doc;
-  int N, mask, window, nd, n_qtiles;
+  int N, mask, window, nd, n_qtiles, bh_count, desc;
   float scale_log2;
 };
 
@@ -43,8 +43,12 @@ __global__ __launch_bounds__(NTF) void fwd_f32_kernel(ParamsF p) {
   __shared__ __attribute__((aligned(16))) float ks[BNF * PITCH];
   __shared__ __attribute__((aligned(16))) float vs[BNF * PITCH];
 
-  const int bh = blockIdx.y;
-  const int qt = blockIdx.x;
+  // costliest first for the masks whose Q tiles cost more the later they
+  // are (tile-major from the last tile down, heads innermost); else in order
+  const int u = blockIdx.x;
+  const int r = u / p.bh_count;
+  const int bh = u - r * p.bh_count;
+  const int qt = p.desc ? p.n_qtiles - 1 - r : r;
   const int tid = threadIdx.x;
   const int row_in = tid >> 1;
   const int half = tid & 1;
@@ -317,8 +321,9 @@ hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_f32_split_kernel<D, OUT_F32>), grid, dim3(NTF), 0, stream, p);
     return hipGetLastError();
   }
-  dim3 grid(p.n_qtiles, a.BH);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, OUT_F32>), grid, dim3(NTF), 0, stream, p);
+  p.bh_count = a.BH;
+  p.desc = (a.mask == MASK_CAUSAL || a.mask == MASK_PREFIX_LM) ? 1 : 0;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, OUT_F32>), dim3(p.n_qtiles * a.BH), dim3(NTF), 0, stream, p);
   return hipGetLastError();
 }
 
