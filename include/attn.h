@@ -92,6 +92,10 @@ typedef enum {
  *             these masks, would be written as 0).
  *   scale   : multiplies Q K^T; the pages use 1/sqrt(d) (kernel listing in
  *             "Flash MSA ...", "Implementation Step-by-Step with Triton").
+ *             Must be positive and finite, else ATTN_ERR_INVALID_ARG (the
+ *             same holds for every entry point below that takes a scale);
+ *             scaled scores must stay finite (inputs whose scores overflow
+ *             fp32 give unspecified results).
  *   mask, window : see attn_mask; window is read by SLIDING, BAND and
  *             PREFIX_LM only.
  *   doc_offsets, num_docs : the documents of DOCUMENT / DOCUMENT_CAUSAL
@@ -116,7 +120,9 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
  * ("FlashAttention-3: Warp Specialization ...", "FP8 Block Quantization").
  *   q8, k8   : [B, H, N, d] OCP E4M3FN bytes.
  *   q_scale, k_scale : [B, H, ceil(N/qk_block)] fp32; the value of element
- *              x is e4m3(code) * scale of its qk_block-row block.
+ *              x is e4m3(code) * scale of its qk_block-row block. Block
+ *              scales must be positive and finite (device contents are not
+ *              checked; others give unspecified results).
  *   v        : [B, H, N, d] bf16.   o : [B, H, N, d] bf16.
  *   S_ij = (sum_k q8_ik k8_jk) * q_scale[i/qk_block] * k_scale[j/qk_block] * scale,
  *   with the fp8 product accumulated in fp32; the rescale is folded into the

@@ -74,6 +74,9 @@ def _fwd(**kw):
     (dict(mask=6, doc=FAKE, nd=0), _lib.ATTN_ERR_INVALID_ARG),
     (dict(mask=5, doc=FAKE + 2, nd=1), _lib.ATTN_ERR_INVALID_ARG),
     (dict(scale=float("nan")), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(scale=-0.125), _lib.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), _lib.ATTN_ERR_INVALID_ARG),
     (dict(B=1 << 16, H=1 << 16, N=1), _lib.ATTN_ERR_INVALID_ARG),
     (dict(lse=FAKE + 2), _lib.ATTN_ERR_INVALID_ARG),
 ])
@@ -96,6 +99,9 @@ def test_attn_fwd_fp8_rejects():
     assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
     bad = list(ok); bad[12] = 5
     assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
+    for scale in (0.0, -0.1, float("inf"), float("nan")):
+        bad = list(ok); bad[11] = scale
+        assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
 
 
 def test_quant_rejects():
@@ -126,6 +132,9 @@ def test_paged_rejects_and_workspace_size():
     assert lib.attn_decode_paged(*bad) == _lib.ATTN_ERR_UNSUPPORTED
     bad = list(ok); bad[11] = 0
     assert lib.attn_decode_paged(*bad) == _lib.ATTN_ERR_INVALID_ARG
+    for scale in (0.0, -0.1, float("inf")):
+        bad = list(ok); bad[12] = scale
+        assert lib.attn_decode_paged(*bad) == _lib.ATTN_ERR_INVALID_ARG
     g = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 16, 8, 20, _lib.ATTN_BF16, None]
     bad = list(g); bad[12] = _lib.ATTN_FP8_E4M3
     assert lib.attn_gather_paged(*bad) == _lib.ATTN_ERR_INVALID_ARG
@@ -158,8 +167,9 @@ def test_paged_prefill_rejects(name):
     assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
     bad = list(ok); bad[1] = FAKE_MIS
     assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
-    bad = list(ok); bad[14] = float("nan")
-    assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
+    for scale in (float("nan"), 0.0, -0.1, float("inf")):
+        bad = list(ok); bad[14] = scale
+        assert f(*bad) == _lib.ATTN_ERR_INVALID_ARG
 
 
 def _expected_class(vis, N, m0, m1, n0, n1):

@@ -53,6 +53,11 @@ attn_status check_dims(int B, int H, int N, int d) {
   return ATTN_OK;
 }
 
+// The kernels give invisible keys a score of -inf before the scale multiplies
+// the scores, and take the running maximum over unscaled scores: both need a
+// positive scale (a zero or negative one would turn -inf into NaN or +inf).
+bool valid_scale(float scale) { return scale > 0.f && scale <= 3.4028234663852886e38f; }
+
 attn_status launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
 }  // namespace
@@ -68,7 +73,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, int B
   if (in_dtype != ATTN_F32 && in_dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
   if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
   if (!valid_mask(mask, window, doc_offsets, num_docs)) return ATTN_ERR_INVALID_ARG;
-  if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_dims(B, H, N, d);
   if (st != ATTN_OK) return st;
   attn::FwdArgs a{};
@@ -98,7 +103,7 @@ static attn_status fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_
     return ATTN_ERR_INVALID_ARG;
   if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
   if (!valid_mask(mask, window, doc_offsets, num_docs)) return ATTN_ERR_INVALID_ARG;
-  if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return ATTN_ERR_INVALID_ARG;
   if (qk_block < 1) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_dims(B, H, N, d);
   if (st != ATTN_OK) return st;
@@ -187,7 +192,7 @@ attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_p
   if (!q || !o) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
   if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
-  if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_paged(k_pool, v_pool, block_table, seq_lens, S, H, d, page_size, max_pages, num_pages);
   if (st != ATTN_OK) return st;
   if (workspace) {
@@ -223,7 +228,7 @@ static attn_status paged_fwd(const void* q, const void* k_pool, const void* v_po
   if (((uintptr_t)table & 3u) || ((uintptr_t)lens & 3u)) return ATTN_ERR_INVALID_ARG;
   if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
   if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
-  if (!(scale == scale)) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return ATTN_ERR_INVALID_ARG;
   if (page_size < 1 || max_pages < 1 || num_pages < 1) return ATTN_ERR_INVALID_ARG;
   attn_status st = check_dims(S, H, q_len, d);
   if (st != ATTN_OK) return st;
