@@ -146,6 +146,17 @@ def dense_inputs(B, H, N, d, seed, outlier_p=0.0, outlier_scale=1.0):
     return q, k, v
 
 
+def dense_inputs_device(B, H, N, d, seed, device="cuda"):
+    """Q, K, V bf16 [B, H, N, d], N(0,1) drawn on the device by a seeded torch
+    generator, for tensors too large to draw on the host. The kernels read
+    them there; the oracle reads host copies of some heads of the same
+    tensors."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return tuple(torch.randn((B, H, N, d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+                 for _ in range(3))
+
+
 def document_offsets(N, l_min, l_max, seed):
     """Document start offsets int32 [num_docs + 1] covering N positions."""
     rng = np.random.default_rng([seed, 1])
