@@ -148,15 +148,20 @@ __global__ __launch_bounds__(NTF) void fwd_f32_kernel(ParamsF p) {
   }
 }
 
-// Small grids (fewer workgroups of 128 rows than CUs): a workgroup owns 32
-// query rows and its four waves split the key tiles among themselves (tile
-// t_lo + j goes to wave j % 4), each wave staging its tiles in its own LDS
-// region, so the waves need no workgroup barrier in the loop. The four
-// partial states (m, l, acc) per row are merged at the end with the same
-// rescale algebra as the split-KV decode. A lane does a quarter of the key
-// work of the 128-row layout, so such a grid finishes sooner.
-constexpr int BMS = 32;  // query rows per workgroup
-constexpr int NWS = 4;   // waves, each taking every fourth key tile
+// Small grids (fewer workgroups of 128 rows than CUs): a workgroup owns 16
+// query rows, four lanes per row (a quarter of d each), and its NW waves
+// split the key tiles among themselves (tile t_lo + j goes to wave j % NW),
+// each wave staging its tiles in its own LDS region, so the waves need no
+// workgroup barrier in the loop. The NW partial states (m, l, acc) per row
+// are merged at the end with the same rescale algebra as the split-KV
+// decode. Against the 128-row layout a lane does 1/16 (d = 64, eight waves)
+// or 1/8 (d = 128, four: the LDS holds no more) of the key work, and the grid
+// has 8x the workgroups, so such a grid finishes sooner.
+constexpr int BMS = 16;  // query rows per workgroup
+constexpr int LPR = 4;   // lanes per query row
+static_assert(BMS * LPR == 64, "one wave covers the workgroup's rows");
+template <int D>
+constexpr int split_waves() { return D == 64 ? 8 : 4; }
 
 // orders the LDS writes of a wave's lanes before their reads by other lanes
 // of the same wave (and the reads before the next writes)
@@ -167,11 +172,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(NTF) void fwd_f32_split_kernel(ParamsF p) {
-  constexpr int HALF = D / 2;
+__global__ __launch_bounds__(64 * split_waves<D>()) void fwd_f32_split_kernel(ParamsF p) {
+  constexpr int NWS = split_waves<D>();
+  constexpr int DQ = D / LPR;   // dims per lane
   constexpr int PITCH = D + 4;  // floats; keeps 16-byte row starts off one bank
   constexpr int TILE = BNF * PITCH;
-  static_assert(64 * (HALF + 2) <= TILE, "a wave's merge record fits its tile region");
+  static_assert(64 * (DQ + 2) <= TILE, "a wave's merge record fits its tile region");
+  static_assert(2 * NWS * TILE * sizeof(float) <= 160 * 1024, "K and V regions fit the LDS");
   __shared__ __attribute__((aligned(16))) float ks[NWS * TILE];
   __shared__ __attribute__((aligned(16))) float vs[NWS * TILE];
 
@@ -180,18 +187,18 @@ __global__ __launch_bounds__(NTF) void fwd_f32_split_kernel(ParamsF p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int half = lane & 1;
+  const int part = lane % LPR;
   const int N = p.N;
   const int m1 = min(m0 + BMS, N);
-  const int qrow = m0 + (lane >> 1);
+  const int qrow = m0 + lane / LPR;
   const size_t head = (size_t)bh * N;
   const RowSpans sp = row_spans(p.mask, p.window, p.doc, p.nd, N, m0, m1 - 1, m0, m1 - 1, min(qrow, N - 1));
 
-  float q[HALF];
-  float acc[HALF];
+  float q[DQ];
+  float acc[DQ];
 #pragma unroll
-  for (int i = 0; i < HALF; ++i) {
-    q[i] = qrow < N ? p.q[(head + qrow) * D + half * HALF + i] : 0.f;
+  for (int i = 0; i < DQ; ++i) {
+    q[i] = qrow < N ? p.q[(head + qrow) * D + part * DQ + i] : 0.f;
     acc[i] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
@@ -222,14 +229,15 @@ __global__ __launch_bounds__(NTF) void fwd_f32_split_kernel(ParamsF p) {
     for (int j = 0; j < BNF; ++j) {
       float dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < HALF; i += 4) {
-        const float4 kk = *(const float4*)(kw + j * PITCH + half * HALF + i);
+      for (int i = 0; i < DQ; i += 4) {
+        const float4 kk = *(const float4*)(kw + j * PITCH + part * DQ + i);
         dot = __builtin_fmaf(q[i], kk.x, dot);
         dot = __builtin_fmaf(q[i + 1], kk.y, dot);
         dot = __builtin_fmaf(q[i + 2], kk.z, dot);
         dot = __builtin_fmaf(q[i + 3], kk.w, dot);
       }
-      dot += __shfl_xor(dot, 1);
+#pragma unroll
+      for (int x = 1; x < LPR; x <<= 1) dot += __shfl_xor(dot, x);
       const int key = n0 + j;
       s[j] = (key >= sp.lane.lo && key <= sp.lane.hi) ? dot : -INFINITY;
     }
@@ -248,12 +256,12 @@ __global__ __launch_bounds__(NTF) void fwd_f32_split_kernel(ParamsF p) {
     l_run = l_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) acc[i] *= alpha;
+    for (int i = 0; i < DQ; ++i) acc[i] *= alpha;
 #pragma unroll
     for (int j = 0; j < BNF; ++j) {
 #pragma unroll
-      for (int i = 0; i < HALF; i += 4) {
-        const float4 vv = *(const float4*)(vw + j * PITCH + half * HALF + i);
+      for (int i = 0; i < DQ; i += 4) {
+        const float4 vv = *(const float4*)(vw + j * PITCH + part * DQ + i);
         acc[i] = __builtin_fmaf(s[j], vv.x, acc[i]);
         acc[i + 1] = __builtin_fmaf(s[j], vv.y, acc[i + 1]);
         acc[i + 2] = __builtin_fmaf(s[j], vv.z, acc[i + 2]);
@@ -265,39 +273,39 @@ __global__ __launch_bounds__(NTF) void fwd_f32_split_kernel(ParamsF p) {
   // merge: each wave leaves (m, l, acc) per lane in its K region; wave 0
   // combines m* = max m_w, l* = sum 2^(m_w - m*) l_w, acc* likewise
   __syncthreads();
-  float* rec = kw + lane * (HALF + 2);
+  float* rec = kw + lane * (DQ + 2);
   rec[0] = m_run;
   rec[1] = l_run;
 #pragma unroll
-  for (int i = 0; i < HALF; ++i) rec[2 + i] = acc[i];
+  for (int i = 0; i < DQ; ++i) rec[2 + i] = acc[i];
   __syncthreads();
   if (wave != 0 || qrow >= N) return;
   float m_star = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < NWS; ++w) m_star = fmaxf(m_star, ks[w * TILE + lane * (HALF + 2)]);
+  for (int w = 0; w < NWS; ++w) m_star = fmaxf(m_star, ks[w * TILE + lane * (DQ + 2)]);
   const float m_use = m_star == -INFINITY ? 0.f : m_star;
   float l_tot = 0.f;
-  float o[HALF];
+  float o[DQ];
 #pragma unroll
-  for (int i = 0; i < HALF; ++i) o[i] = 0.f;
+  for (int i = 0; i < DQ; ++i) o[i] = 0.f;
 #pragma unroll
   for (int w = 0; w < NWS; ++w) {
-    const float* r = ks + w * TILE + lane * (HALF + 2);
+    const float* r = ks + w * TILE + lane * (DQ + 2);
     const float wt = exp2f(r[0] - m_use);
     l_tot += wt * r[1];
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) o[i] += wt * r[2 + i];
+    for (int i = 0; i < DQ; ++i) o[i] += wt * r[2 + i];
   }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-  for (int i = 0; i < HALF; ++i) {
+  for (int i = 0; i < DQ; ++i) {
     const float x = o[i] * inv;
     if constexpr (OUT_F32)
-      ((float*)p.o)[(head + qrow) * D + half * HALF + i] = x;
+      ((float*)p.o)[(head + qrow) * D + part * DQ + i] = x;
     else
-      ((__bf16*)p.o)[(head + qrow) * D + half * HALF + i] = (__bf16)x;
+      ((__bf16*)p.o)[(head + qrow) * D + part * DQ + i] = (__bf16)x;
   }
-  if (p.lse != nullptr && half == 0)
+  if (p.lse != nullptr && part == 0)
     p.lse[head + qrow] = l_tot > 0.f ? (m_star + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
@@ -318,7 +326,7 @@ hipError_t launch_f32_d(const FwdArgs& a, hipStream_t stream) {
   p.scale_log2 = a.scale * kLog2e;
   if ((long long)p.n_qtiles * a.BH < kSmallGridWorkgroups) {
     dim3 grid((a.N + BMS - 1) / BMS, a.BH);
-    hipLaunchKernelGGL((fwd_f32_split_kernel<D, OUT_F32>), grid, dim3(NTF), 0, stream, p);
+    hipLaunchKernelGGL((fwd_f32_split_kernel<D, OUT_F32>), grid, dim3(64 * split_waves<D>()), 0, stream, p);
     return hipGetLastError();
   }
   p.bh_count = a.BH;
