@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <cmath>
+
 #include "attn_common.h"
 #include "launch.h"
 
@@ -56,7 +58,7 @@ attn_status check_dims(int B, int H, int N, int d) {
 // The kernels give invisible keys a score of -inf before the scale multiplies
 // the scores, and take the running maximum over unscaled scores: both need a
 // positive scale (a zero or negative one would turn -inf into NaN or +inf).
-bool valid_scale(float scale) { return scale > 0.f && scale <= 3.4028234663852886e38f; }
+bool valid_scale(float scale) { return scale > 0.f && std::isfinite(scale); }
 
 attn_status launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
