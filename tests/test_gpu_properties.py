@@ -2,8 +2,9 @@
 
 The oracle is pinned to these same properties; here they are asserted on the
 kernels directly, as a second check that does not go through the oracle.
-The attention the pages define (FlashAttention-2 paper, "Standard attention
-implementation"; the online softmax of its forward pass):
+The attention the pages define ("Flash MSA Attention Kernel Implementation
+Tutorial", "Understanding Flash MSA Core Mechanics": softmax of the scaled
+scores times V, computed with an online softmax) implies:
 - with every score equal (all keys zero, so every score is 0), softmax
   weights are uniform: a row's output is the mean of the V rows it sees and
   its LSE is the log of their count, for any Q and under every mask;
