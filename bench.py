@@ -367,8 +367,9 @@ def main():
                     help="first run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the kernels shard by head or sequence with no exchange, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (attention shards by "
+              "head or by sequence with no exchange, so one GPU's throughput is the per-GPU figure)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
