@@ -18,7 +18,9 @@ carries:
                   sequences, two-sided window, prefix-LM and the unmasked
                   shape the document masks are compared with), each timed
                   with HIP events.
-One GPU only: --gpus above 1 exits with a message.
+With --sweep it instead prints one JSON line of bf16 prefill rates over
+sequence length (causal and unmasked, d = 64 and 128, 16 heads), for context
+beside the fixed workloads. One GPU only: --gpus above 1 exits with a message.
 """
 
 import argparse
@@ -351,6 +353,32 @@ def wl_keys():
     return wl.WORKLOADS.keys()
 
 
+def seq_len_sweep(torch, A):
+    """bf16 prefill over N = 1K..32K: B = 4*2048^2/N^2 (at least 1) by 16
+    heads, so N <= 2048 carries the causal workload's work per launch.
+    Inputs N(0,1) drawn on the device (seeded); each line is timed with HIP
+    events after settling launches."""
+    rows = []
+    for d in (64, 128):
+        for mask in ("causal", "none"):
+            for N in (1024, 2048, 4096, 8192, 16384, 32768):
+                B, H = max(1, (4 * 2048 * 2048) // (N * N)), 16
+                g = torch.Generator(device="cuda")
+                g.manual_seed(N + d)
+                q, k, v = (torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+                           for _ in range(3))
+                o = torch.empty_like(q)
+                step = lambda: A.attn_fwd(q, k, v, o, 1.0 / math.sqrt(d), mask)
+                ms, _, _ = event_time_ms(step, 20 if N <= 8192 else 5)
+                pairs = N * (N + 1) / 2 if mask == "causal" else N * N
+                tf = 4.0 * d * B * H * pairs / ms / 1e9
+                rows.append({"d": d, "mask": mask, "N": N, "B": B, "H": H, "ms": round(ms, 5),
+                             "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+                log(f"sweep: d={d} {mask} N={N}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+                del q, k, v, o
+    return {"sweep": "bf16 prefill TFLOP/s over sequence length", "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +391,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=sorted(wl_keys()),
                     help="workload for --only-main runs (profiling); the JSON line always reports 2 otherwise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="print bf16 prefill TFLOP/s over sequence length instead of the benchmark line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -379,6 +409,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if args.sweep:
+        print(json.dumps(seq_len_sweep(torch, A)))
+        return
 
     def make(key):
         seed = args.seed if args.seed is not None else wl.default_seed(key)
