@@ -7,7 +7,8 @@
 // lanes share a row (each holds half of q and of the accumulator), so the
 // running m and l of a row are computed redundantly in both lanes and never
 // leave registers. K/V tiles of 32 keys are staged in LDS and read as
-// broadcasts (all lanes of a half read the same address).
+// broadcasts (all lanes of a half read the same address). Grids too small to
+// fill the chip run a split-key layout instead (below).
 #include <type_traits>
 
 #include "attn_common.h"
