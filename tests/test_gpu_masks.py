@@ -160,7 +160,7 @@ def _sampled_full_size(key, heads):
 
 
 @pytest.mark.parametrize("key,heads", [(6, [(0, 0), (0, 15)]), (7, [(0, 3), (0, 12)]), (8, [(0, 0), (0, 9)]),
-                                       (9, [(0, 0), (1, 15)])])
+                                       (9, [(0, 0), (1, 15)]), (10, [(0, 0), (0, 11)])])
 def test_structured_workloads_full_size_sampled(key, heads):
     _sampled_full_size(key, heads)
 
