@@ -302,6 +302,19 @@ attn_status attn_k_tile_range(attn_mask mask, int window, const int32_t* doc_off
 attn_status attn_full_tile_range(attn_mask mask, int window, const int32_t* doc_offsets, int num_docs,
                                  int N, int m0, int m1, int bn, int* f_lo, int* f_hi);
 
+/* Host copy of the heaviest-first dispatch ranking that the document-masked
+ * and paged prefill kernels compute on the device (the same code): groups of
+ * work (query tiles, sequences) are ranked by cost, descending, ties by
+ * index, and workgroup id r takes the group of rank r, so the hardware's
+ * in-order dispatch runs the costliest first (the longest-first rule for
+ * load balance; the pages' Pattern A, "Optimizing Triton kernels ...",
+ * notes that a document mask makes tile costs uneven).
+ *   costs : host int32 [groups], each in [0, 2^23).   groups : 1 .. 256.
+ *   ranks : host int32 [groups] out; ranks[g] = number of groups ranked
+ *           before group g.
+ * Returns ATTN_ERR_INVALID_ARG for other arguments. */
+attn_status attn_dispatch_ranks(const int32_t* costs, int groups, int32_t* ranks);
+
 const char* attn_status_str(attn_status s);
 int attn_abi_version(void);
 

@@ -267,3 +267,155 @@ def test_tile_counts_at_workload_sizes():
     assert pairs("sliding", 4096, 8192) == 3168
     assert pairs("causal", 0, 16384) == 16512
     assert pairs("none", 0, 256) == 8
+
+
+def _expected_ranks(costs):
+    """Heaviest first, ties by index: the rank of g is the number of groups
+    with a larger cost, or an equal cost and a lower index."""
+    order = sorted(range(len(costs)), key=lambda g: (-costs[g], g))
+    ranks = [0] * len(costs)
+    for r, g in enumerate(order):
+        ranks[g] = r
+    return ranks
+
+
+def test_dispatch_ranks_are_the_heaviest_first_permutation_for_every_group_count():
+    """The device ranking's code (shared with this host copy) reads only the
+    keys it wrote, padded to whole rounds of sixteen, and its ranks are a
+    permutation for every group count 1..256: a bound that counted keys past
+    the written ones once left order slots unset on the GPU."""
+    rng = np.random.default_rng(7)
+    for g in range(1, 257):
+        for costs in (rng.integers(0, 64, size=g), rng.integers(0, 1 << 23, size=g), np.zeros(g, dtype=int),
+                      np.full(g, (1 << 23) - 1)):
+            costs = [int(c) for c in costs]
+            ranks = _lib.attn_dispatch_ranks(costs)
+            assert sorted(ranks) == list(range(g)), g
+            assert ranks == _expected_ranks(costs), g
+
+
+def test_dispatch_ranks_reject_bad_arguments():
+    lib = _lib.load()
+    arr = (ctypes.c_int32 * 300)()
+    out = (ctypes.c_int32 * 300)()
+    assert lib.attn_dispatch_ranks(arr, 0, out) == _lib.ATTN_ERR_INVALID_ARG
+    assert lib.attn_dispatch_ranks(arr, 257, out) == _lib.ATTN_ERR_INVALID_ARG
+    assert lib.attn_dispatch_ranks(None, 4, out) == _lib.ATTN_ERR_INVALID_ARG
+    assert lib.attn_dispatch_ranks(arr, 4, None) == _lib.ATTN_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        _lib.attn_dispatch_ranks([1, -1])
+    with pytest.raises(ValueError):
+        _lib.attn_dispatch_ranks([1 << 23])
+
+
+# ------------------------------------------------ binding argument validation
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _binding_cases():
+    """(name, call, bad argument) triples: each call has exactly one tensor of
+    the wrong shape or dtype, which the binding must refuse before the library
+    sees it (no kernel is launched: these are host tensors)."""
+    import torch
+    f32, bf16, u8, i32 = torch.float32, torch.bfloat16, torch.uint8, torch.int32
+    B, H, N, d = 1, 2, 130, 64
+    q = _t((B, H, N, d), bf16)
+    cases = []
+
+    def fwd(**kw):
+        a = dict(q=q, k=q, v=q, o=_t((B, H, N, d), f32), lse=None)
+        a.update(kw)
+        return lambda: _lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], 0.1, "causal", lse=a["lse"])
+    cases += [("attn_fwd ok", fwd(), None),
+              ("lse shape", fwd(lse=_t((B, H), f32)), "lse"),
+              ("lse dtype", fwd(lse=_t((B, H, N), bf16)), "lse"),
+              ("k shape", fwd(k=_t((B, H, N + 1, d), bf16)), "k"),
+              ("v dtype", fwd(v=_t((B, H, N, d), f32)), "v"),
+              ("o shape", fwd(o=_t((B, H, N, 2 * d), f32)), "o")]
+    cases.append(("doc offsets dtype",
+                  lambda: _lib.attn_fwd(q, q, q, q, 0.1, "document", doc_offsets=_t((3,), torch.int64)),
+                  "doc_offsets"))
+
+    nb = 2
+    def fp8(**kw):
+        a = dict(q8=_t((B, H, N, d), u8), sq=_t((B, H, nb), f32), k8=_t((B, H, N, d), u8), sk=_t((B, H, nb), f32),
+                 v=q, o=_t((B, H, N, d), bf16), lse=None, v8=None, sv=None)
+        a.update(kw)
+        if a["v8"] is not None:
+            return lambda: _lib.attn_fwd_fp8_full(a["q8"], a["sq"], a["k8"], a["sk"], a["v8"], a["sv"], a["o"], 0.1,
+                                                  "causal", lse=a["lse"])
+        return lambda: _lib.attn_fwd_fp8(a["q8"], a["sq"], a["k8"], a["sk"], a["v"], a["o"], 0.1, "causal",
+                                         lse=a["lse"])
+    cases += [("fp8 ok", fp8(), None),
+              ("q_scale shape", fp8(sq=_t((B, H, nb + 1), f32)), "q_scale"),
+              ("k_scale dtype", fp8(sk=_t((B, H, nb), bf16)), "k_scale"),
+              ("k8 dtype", fp8(k8=_t((B, H, N, d), bf16)), "k8"),
+              ("fp8 lse", fp8(lse=_t((B, H, N, 1), f32)), "lse"),
+              ("fp8 full ok", fp8(v8=_t((B, H, N, d), u8), sv=_t((B, H, nb), f32)), None),
+              ("v_scale shape", fp8(v8=_t((B, H, N, d), u8), sv=_t((B, H), f32)), "v_scale"),
+              ("v8 dtype", fp8(v8=_t((B, H, N, d), bf16), sv=_t((B, H, nb), f32)), "v8")]
+
+    x = _t((B, H, N, d), f32)
+    cases += [("quant ok", lambda: _lib.attn_quant_fp8_block(x, _t((B, H, N, d), u8), _t((B, H, nb), f32)), None),
+              ("quant codes", lambda: _lib.attn_quant_fp8_block(x, _t((B, H, N, d), f32), _t((B, H, nb), f32)),
+               "codes"),
+              ("quant scales", lambda: _lib.attn_quant_fp8_block_pow2(x, _t((B, H, N, d), u8), _t((B, H, 1), f32)),
+               "scales")]
+
+    S, P, pg, mp = 3, 10, 16, 4
+    pool = _t((P, H, pg, d), bf16)
+    def dec(**kw):
+        a = dict(q=_t((S, H, d), bf16), kp=pool, vp=pool, bt=_t((S, mp), i32), lens=_t((S,), i32),
+                 o=_t((S, H, d), bf16), lse=None)
+        a.update(kw)
+        return lambda: _lib.attn_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["lens"], a["o"], 0.1,
+                                              lse=a["lse"])
+    cases += [("decode ok", dec(), None),
+              ("decode lse", dec(lse=_t((S,), f32)), "lse"),
+              ("decode table dtype", dec(bt=_t((S, mp), torch.int64)), "block_table"),
+              ("decode table rows", dec(bt=_t((S + 1, mp), i32)), "block_table"),
+              ("decode lens", dec(lens=_t((S, 1), i32)), "seq_lens"),
+              ("decode pool heads", dec(kp=_t((P, H + 1, pg, d), bf16)), "k_pool"),
+              ("decode v pool", dec(vp=_t((P, H, pg, d), f32)), "v_pool")]
+
+    ql = 200
+    qb = 2
+    def pre(cross=False, **kw):
+        a = dict(q=_t((S, H, ql, d), bf16), kp=pool, vp=pool,
+                 t=_t((S, qb, mp) if cross else (S, mp), i32), l=_t((S, qb) if cross else (S,), i32),
+                 o=_t((S, H, ql, d), bf16), lse=None)
+        a.update(kw)
+        fn = _lib.attn_cross_paged if cross else _lib.attn_prefill_paged
+        return lambda: fn(a["q"], a["kp"], a["vp"], a["t"], a["l"], a["o"], 0.1, lse=a["lse"])
+    cases += [("prefill ok", pre(), None),
+              ("prefill lse", pre(lse=_t((S, H), f32)), "lse"),
+              ("prefill table", pre(t=_t((S, qb, mp), i32)), "block_table"),
+              ("cross ok", pre(cross=True), None),
+              ("cross decode-style table", pre(cross=True, t=_t((S, mp), i32)), "page_table"),
+              ("cross lens", pre(cross=True, l=_t((S,), i32)), "kv_lens"),
+              ("cross o dtype", pre(cross=True, o=_t((S, H, ql, d), u8)), "o")]
+
+    def gat(**kw):
+        a = dict(kp=pool, vp=pool, bt=_t((S, mp), i32), lens=_t((S,), i32), ko=_t((S, H, mp * pg, d), bf16),
+                 vo=_t((S, H, mp * pg, d), bf16))
+        a.update(kw)
+        return lambda: _lib.attn_gather_paged(a["kp"], a["vp"], a["bt"], a["lens"], a["ko"], a["vo"])
+    cases += [("gather ok", gat(), None),
+              ("gather out rows", gat(ko=_t((S, H, mp * pg - 1, d), bf16)), "k_out"),
+              ("gather out dtype", gat(vo=_t((S, H, mp * pg, d), f32)), "v_out")]
+    return cases
+
+
+@pytest.mark.parametrize("case", _binding_cases(), ids=lambda c: c[0])
+def test_binding_checks_every_tensor_argument(case):
+    name, call, bad = case
+    if bad is None:
+        # every shape and dtype is right: only the device check remains
+        with pytest.raises(ValueError, match="GPU tensors"):
+            call()
+    else:
+        with pytest.raises(ValueError, match=rf"^{bad} must"):
+            call()

@@ -352,6 +352,25 @@ attn_status attn_full_tile_range(attn_mask mask, int window, const int32_t* doc_
   return ATTN_OK;
 }
 
+attn_status attn_dispatch_ranks(const int32_t* costs, int groups, int32_t* ranks) {
+  if (!costs || !ranks || groups < 1 || groups > attn::kRankMaxGroups) return ATTN_ERR_INVALID_ARG;
+  for (int g = 0; g < groups; ++g)
+    if (costs[g] < 0 || costs[g] >= (1 << 23)) return ATTN_ERR_INVALID_ARG;
+  // the workgroup's key array, as its threads fill it
+  alignas(16) int keys[attn::kRankMaxGroups];
+  const int padded = attn::rank_padded(groups);
+  for (int t = 0; t < padded; ++t) keys[t] = t < groups ? (int)attn::rank_key(costs[t], t) : 0;
+  for (int g = 0; g < groups; ++g) ranks[g] = 0;
+  // every counting thread in turn (their sums do not depend on the order)
+  const int parts = attn::rank_parts(groups, attn::kRankMaxGroups);
+  for (int t = 0; t < parts * groups; ++t) {
+    const int part = attn::rank_part(t, groups);
+    const int g = t - part * groups;
+    ranks[g] += attn::rank_count((const attn::i32x4*)keys, groups, part, parts, (unsigned)keys[g]);
+  }
+  return ATTN_OK;
+}
+
 const char* attn_status_str(attn_status s) {
   switch (s) {
     case ATTN_OK: return "ATTN_OK";

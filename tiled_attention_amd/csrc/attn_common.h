@@ -205,4 +205,37 @@ __device__ inline int xcd_unit(int wg, int grid) {
 
 __host__ inline int round_up8(int x) { return (x + 7) & ~7; }
 
+// Heaviest-first ranking of G <= 256 groups of work by cost (descending,
+// ties by group index), shared by the kernels that order their dispatch and
+// by a host copy that tests it. Group g's key is (cost + 1) * 256 + (255 - g):
+// distinct per group, larger for a larger cost and, at equal cost, for a
+// lower index; costs must lie in [0, 2^23). The keys are stored padded with
+// zeros (below every key) to a multiple of sixteen, and a group's rank is the
+// number of keys above its own, counted sixteen at a time by `parts`
+// threads, each taking every parts-th round of sixteen.
+constexpr int kRankMaxGroups = 256;   // one thread per group in a 256-thread workgroup
+__host__ __device__ inline unsigned rank_key(int cost, int g) {
+  return (unsigned)(cost + 1) * 256u + (unsigned)(255 - g);
+}
+__host__ __device__ inline int rank_padded(int G) { return (G + 15) & ~15; }
+__host__ __device__ inline int rank_parts(int G, int threads) {
+  return G <= threads / 4 ? 4 : G <= threads / 2 ? 2 : 1;
+}
+// part of thread t (t < parts * G) and the group it counts for: t = part * G + g
+__host__ __device__ inline int rank_part(int t, int G) { return (t >= G) + (t >= 2 * G) + (t >= 3 * G); }
+// keys above `key` in rounds part, part + parts, ... of the padded keys
+// (keys4: the padded keys as 16-byte vectors, rank_padded(G) / 4 of them)
+__host__ __device__ inline int rank_count(const i32x4* keys4, int G, int part, int parts, unsigned key) {
+  int r = 0;
+  const int n16 = rank_padded(G) >> 4;
+  for (int round = part; round < n16; round += parts) {
+    const i32x4 v0 = keys4[4 * round], v1 = keys4[4 * round + 1], v2 = keys4[4 * round + 2],
+                v3 = keys4[4 * round + 3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r += ((unsigned)v0[e] > key) + ((unsigned)v1[e] > key) + ((unsigned)v2[e] > key) + ((unsigned)v3[e] > key);
+  }
+  return r;
+}
+
 }  // namespace attn

@@ -227,9 +227,13 @@ __device__ __forceinline__ void sync_tiles() {
 // the end of the sequence (so rows >= N load as zeros).
 struct TileStream {
   uint64_t base;    // global address of the next tile to issue
-  int remain;       // bytes from base to the end of the head (may go <= 0)
+  int64_t remain;   // bytes from base to the end of the head (may go <= 0; a head
+                    // can hold 2^31 or more bytes)
+  // The size field is 32 bits: past 2^31 - 1 it is clamped, which loses
+  // nothing, since one issue reads at most one tile (< 2^31 bytes) past base.
   __device__ __forceinline__ i32x4 rsrc() const {
-    return (i32x4){(int)(uint32_t)base, (int)(uint32_t)(base >> 32), remain > 0 ? remain : 0, kBufferFlags};
+    const int n = remain <= 0 ? 0 : remain >= 0x7fffffff ? 0x7fffffff : (int)remain;
+    return (i32x4){(int)(uint32_t)base, (int)(uint32_t)(base >> 32), n, kBufferFlags};
   }
 };
 
@@ -424,13 +428,13 @@ struct QTile {
     lds_v = __builtin_amdgcn_readfirstlane(lds0 + NS * C::K_SLOT + wave * 1024);
     const uint64_t kb = PG ? 0 : (uint64_t)(uintptr_t)p.k + (head + (size_t)t_lo * BN) * KROW;
     const uint64_t vb = PG ? 0 : (uint64_t)(uintptr_t)p.v + (head + (size_t)t_lo * BN) * VROW;
-    const int rem = N - t_lo * BN;
+    const int rem = __builtin_amdgcn_readfirstlane(N - t_lo * BN);
     ks.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kb >> 32)) << 32) |
               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kb);
     vs.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(vb >> 32)) << 32) |
               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)vb);
-    ks.remain = __builtin_amdgcn_readfirstlane(rem * KROW);
-    vs.remain = __builtin_amdgcn_readfirstlane(rem * VROW);
+    ks.remain = (int64_t)rem * KROW;
+    vs.remain = (int64_t)rem * VROW;
 
     m_ref = -INFINITY;
     m_use = 0.f;
@@ -938,12 +942,11 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
     } else {
       c = min(max(p.pg_lens[tid], 0), p.pg_max * p.pg_page);
     }
-    // one key per group orders by cost, then by index: (cost + 1) * 256 +
-    // (255 - group); keys are distinct, costs stay below 2^23
-    cost[tid] = (c + 1) * 256 + (255 - tid);
+    // the ranking's key (attn_common.h): by cost, then by index
+    cost[tid] = (int)rank_key(c, tid);
     order[tid] = 0;                        // rank counter of group tid
-  } else if (tid < ((G + 15) & ~15)) {
-    cost[tid] = 0;                         // padding to whole 64-byte rounds; below every key
+  } else if (tid < rank_padded(G)) {
+    cost[tid] = 0;                         // padding to whole rounds of sixteen; below every key
   }
   __syncthreads();
   // rank = number of larger keys. The keys are read sixteen at a time (four
@@ -951,20 +954,11 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
   // groups two or four threads share a group's rounds and add their counts:
   // one read per group in turn took about 8000 cycles at 128 groups, and
   // every workgroup ranks all groups.
-  const int parts = G <= NT / 4 ? 4 : G <= NT / 2 ? 2 : 1;
+  const int parts = rank_parts(G, NT);
   if (tid < parts * G) {
-    const int part = (tid >= G) + (tid >= 2 * G) + (tid >= 3 * G);
+    const int part = rank_part(tid, G);
     const int g = tid - part * G;
-    const unsigned key = (unsigned)cost[g];
-    int r = 0;
-    const i32x4* c4 = (const i32x4*)cost;
-    const int n16 = (G + 15) >> 4;         // rounds of sixteen keys over the padded keys
-    for (int round = part; round < n16; round += parts) {
-      const i32x4 v0 = c4[4 * round], v1 = c4[4 * round + 1], v2 = c4[4 * round + 2], v3 = c4[4 * round + 3];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r += ((unsigned)v0[e] > key) + ((unsigned)v1[e] > key) + ((unsigned)v2[e] > key) + ((unsigned)v3[e] > key);
-    }
+    const int r = rank_count((const i32x4*)cost, G, part, parts, (unsigned)cost[g]);
     atomicAdd(&order[g], r);
   }
   __syncthreads();
