@@ -28,6 +28,21 @@ LSE_TOL_MFMA = 2.5e-3
 LSE_REL_TOL_FP8 = 2e-3
 
 
+def check_lse(got, ref, tol=None, what=""):
+    """max |LSE_gpu - LSE_ref| over the finite rows <= tol (default
+    LSE_TOL_MFMA); rows with no visible key must be -inf on both sides. The
+    error is printed so a run's log records the margin."""
+    tol = LSE_TOL_MFMA if tol is None else tol
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    live = np.isfinite(ref)
+    assert np.all(got[~live] == -np.inf), f"{what}: LSE of a row with no key"
+    err = float(np.max(np.abs(got[live] - ref[live]))) if live.any() else 0.0
+    say(f"LSE max abs err {err:.3g} (tol {tol:.3g}) {what}")
+    assert err <= tol, f"{what}: LSE max abs err {err:.3g} > {tol:.3g}"
+    return err
+
+
 def check_lse_fp8(got, ref):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from parity import LSE_TOL_MFMA, check_close, cuda, sample_rows, say, to_np
+from parity import check_lse, LSE_TOL_MFMA, check_close, cuda, sample_rows, say, to_np
 from tiled_attention_amd import _lib as A
 from tiled_attention_amd import workloads as wl
 
@@ -45,7 +45,7 @@ def test_fwd_bf16_small_elementwise(case, out):
     ref, ref_lse = oracle.attention(wl.bf16_to_f64(qb), wl.bf16_to_f64(kb), wl.bf16_to_f64(vb), scale, mask,
                                     window if mask == "sliding" else None)
     check_close(to_np(o), ref, out == "bf16", what=str(case))
-    assert np.max(np.abs(to_np(lse) - ref_lse)) <= LSE_TOL_MFMA
+    check_lse(to_np(lse), ref_lse)
 
 
 @pytest.mark.parametrize("case", [(1, 1, 256, 64, "none", 0), (1, 2, 77, 64, "causal", 0),
@@ -62,7 +62,7 @@ def test_fwd_f32_elementwise(case):
                                     window if mask == "sliding" else None)
     err = check_close(to_np(o), ref, False, what=str(case))
     assert err <= 1e-4, err            # fp32 throughout: far inside the 1e-2 bar
-    assert np.max(np.abs(to_np(lse) - ref_lse)) <= 1e-4
+    check_lse(to_np(lse), ref_lse, tol=1e-4)
 
 
 @pytest.mark.parametrize("case", [(2, 8, 4096, 64, "causal"), (1, 16, 2100, 128, "none")],
@@ -81,7 +81,7 @@ def test_fwd_f32_large_grid_sampled(case):
         ref, ref_lse = oracle.attention(q[b, h].numpy(), k[b, h].numpy(), v[b, h].numpy(), scale, mask, rows=rows)
         err = check_close(to_np(o[b, h][rows]), ref, False, what=f"{case} {(b, h)}")
         assert err <= 1e-4, err
-        assert np.max(np.abs(to_np(lse[b, h][rows]) - ref_lse)) <= 1e-4
+        check_lse(to_np(lse[b, h][rows]), ref_lse, tol=1e-4)
 
 
 def test_fwd_f32_workload_1_full():
@@ -113,7 +113,7 @@ def _sampled_full_size(key, heads, seed):
                                         window or None, rows=rows)
         worst = max(worst, check_close(to_np(o32[b, h][rows]), ref, False, what=f"{w.name} f32 {(b, h)}"))
         check_close(to_np(o_bf[b, h][rows]), ref, True, what=f"{w.name} bf16 {(b, h)}")
-        assert np.max(np.abs(to_np(lse[b, h][rows]) - ref_lse)) <= LSE_TOL_MFMA
+        check_lse(to_np(lse[b, h][rows]), ref_lse)
     say(f"{w.name}: sampled max abs err (fp32 out) {worst:.3g}")
     return qb, kb, vb, o_bf
 

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from parity import LSE_TOL_MFMA, check_close, cuda, sample_rows, say, to_np
+from parity import check_lse, LSE_TOL_MFMA, check_close, cuda, sample_rows, say, to_np
 from tiled_attention_amd import _lib as A
 from tiled_attention_amd import workloads as wl
 
@@ -42,7 +42,7 @@ def test_long_sequence_bf16_sampled(d, mask):
     ref, ref_lse = oracle.attention(wl.bf16_to_f64(qb[0, 0]), wl.bf16_to_f64(kb[0, 0]), wl.bf16_to_f64(vb[0, 0]),
                                     scale, mask, rows=rows)
     err = check_close(to_np(o[0, 0][rows]), ref, False, what=f"N={N} d={d} {mask}")
-    assert np.max(np.abs(to_np(lse[0, 0][rows]) - ref_lse)) <= LSE_TOL_MFMA
+    check_lse(to_np(lse[0, 0][rows]), ref_lse)
     say(f"long bf16: sampled max abs err {err:.3g}")
 
 
@@ -61,7 +61,7 @@ def test_tensors_past_32_bit_offsets():
         qh, kh, vh = (wl.bf16_to_f64(x[0, h].cpu()) for x in (qd, kd, vd))
         ref, ref_lse = oracle.attention(qh, kh, vh, 1.0 / math.sqrt(d), "causal", rows=rows)
         err = check_close(to_np(o[0, h][rows]), ref, True, what=f"head {h}")
-        assert np.max(np.abs(to_np(lse[0, h][rows]) - ref_lse)) <= LSE_TOL_MFMA
+        check_lse(to_np(lse[0, h][rows]), ref_lse)
         say(f"large tensors: head {h} sampled max abs err {err:.3g}")
 
 
@@ -76,7 +76,7 @@ def test_long_sequence_f32_causal_sampled():
     ref, ref_lse = oracle.attention(q[0, 0].numpy(), k[0, 0].numpy(), v[0, 0].numpy(), 0.125, "causal", rows=rows)
     err = check_close(to_np(o[0, 0][rows]), ref, False, what="fp32 long causal")
     assert err <= 1e-4
-    assert np.max(np.abs(to_np(lse[0, 0][rows]) - ref_lse)) <= 1e-4
+    check_lse(to_np(lse[0, 0][rows]), ref_lse, tol=1e-4)
 
 
 @pytest.mark.parametrize("page", [16, 64])
@@ -96,4 +96,28 @@ def test_long_decode(page):
     ref, ref_lse = oracle.decode(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
                                  inp.block_table.numpy(), inp.seq_lens.numpy(), 1.0 / math.sqrt(d), page_size=page)
     check_close(to_np(o), ref, True, what=f"decode L={L} page={page}")
-    assert np.max(np.abs(to_np(lse) - ref_lse)) <= 1e-3
+    check_lse(to_np(lse), ref_lse, tol=1e-3)
+
+
+def test_head_of_more_than_2gib_of_bytes():
+    """One head of 2^23 + 77 keys at d = 128: K and V hold more than 2^31
+    bytes per head, so the byte count a K/V tile stream has left from the
+    first tiles does not fit 32 bits. A one-sided 100-key window keeps the
+    work small; rows near the start (where that count is largest), the middle
+    and the end are checked against the oracle on the keys their window
+    covers."""
+    N, d, W = (1 << 23) + 77, 128, 100
+    say(f"2 GiB head: [1,1,{N},{d}] bf16 drawn on the device, window {W}")
+    qd, kd, vd = wl.dense_inputs_device(1, 1, N, d, seed=9191)
+    o = torch.empty_like(qd)
+    A.attn_fwd(qd, kd, vd, o, 1.0 / math.sqrt(d), "sliding", W)
+    torch.cuda.synchronize()
+    say("2 GiB head: checking rows")
+    worst = 0.0
+    for r0 in (0, 191, N // 2 - 64, N - 300):
+        r1 = min(r0 + 300, N)
+        a = max(0, r0 - W + 1)
+        qh, kh, vh = (wl.bf16_to_f64(x[0, 0, lo:r1].cpu()) for x, lo in ((qd, r0), (kd, a), (vd, a)))
+        ref, _ = oracle.attention(qh, kh, vh, 1.0 / math.sqrt(d), "sliding", W, q_pos_offset=r0 - a)
+        worst = max(worst, check_close(to_np(o[0, 0, r0:r1]), ref, True, what=f"rows {r0}..{r1}"))
+    say(f"2 GiB head: max abs err {worst:.3g}")

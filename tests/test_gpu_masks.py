@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from parity import FP8_REL_RMSE, LSE_TOL_MFMA, check_close, cuda, rel_rmse, sample_rows, say, to_np
+from parity import check_lse, FP8_REL_RMSE, LSE_TOL_MFMA, check_close, cuda, rel_rmse, sample_rows, say, to_np
 from tiled_attention_amd import _lib as A
 from tiled_attention_amd import workloads as wl
 
@@ -83,7 +83,7 @@ def test_masks_bf16_small_elementwise(case, out):
     o, lse = _run(qb, kb, vb, scale, mask, window, torch.float32 if out == "f32" else torch.bfloat16, offs)
     ref, ref_lse = _ref(qb, kb, vb, scale, mask, window, offs)
     check_close(to_np(o), ref, out == "bf16", what=str(case))
-    assert np.max(np.abs(to_np(lse) - ref_lse)) <= LSE_TOL_MFMA
+    check_lse(to_np(lse), ref_lse)
 
 
 @pytest.mark.parametrize("case", [(1, 1, 256, 64, "band", 3, None), (1, 2, 300, 128, "prefix_lm", 40, None),
@@ -104,7 +104,7 @@ def test_masks_f32_elementwise(case):
                                     doc_offsets=None if offs is None else np.asarray(offs))
     err = check_close(to_np(o), ref, False, what=str(case))
     assert err <= 1e-4, err
-    assert np.max(np.abs(to_np(lse) - ref_lse)) <= 1e-4
+    check_lse(to_np(lse), ref_lse, tol=1e-4)
 
 
 def test_document_masks_fp8():
@@ -155,7 +155,7 @@ def _sampled_full_size(key, heads):
         ref, ref_lse = _ref(qb[b, h], kb[b, h], vb[b, h], w.scale, w.mask, w.window, offs, rows=rows)
         worst = max(worst, check_close(to_np(o32[b, h][rows]), ref, False, what=f"{w.name} f32 {(b, h)}"))
         check_close(to_np(o_bf[b, h][rows]), ref, True, what=f"{w.name} bf16 {(b, h)}")
-        assert np.max(np.abs(to_np(lse[b, h][rows]) - ref_lse)) <= LSE_TOL_MFMA
+        check_lse(to_np(lse[b, h][rows]), ref_lse)
     say(f"{w.name}: sampled max abs err (fp32 out) {worst:.3g}")
 
 

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from parity import LSE_TOL_MFMA, check_close, sample_rows, say, to_np
+from parity import check_lse, LSE_TOL_MFMA, check_close, sample_rows, say, to_np
 from tiled_attention_amd import _lib as A
 from tiled_attention_amd import workloads as wl
 
@@ -48,7 +48,7 @@ def test_prefill_paged_small_elementwise(case, out, page):
     ref, ref_lse = oracle.prefill(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
                                   inp.block_table.numpy(), inp.seq_lens.numpy(), scale, page_size=page)
     check_close(to_np(o), ref, out == "bf16", what=str(case))
-    assert np.max(np.abs(to_np(lse) - ref_lse)) <= LSE_TOL_MFMA
+    check_lse(to_np(lse), ref_lse)
 
 
 def _cross(inp, out_dtype, scale):
@@ -80,10 +80,7 @@ def test_cross_paged_small_elementwise(case, out, page):
     ref, ref_lse = oracle.cross(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
                                 inp.page_table.numpy(), inp.kv_lens.numpy(), scale, page_size=page)
     check_close(to_np(o), ref, out == "bf16", what=str(case))
-    got_lse = to_np(lse)
-    live = np.isfinite(ref_lse)
-    assert np.all(got_lse[~live] == -np.inf)
-    assert np.max(np.abs(got_lse[live] - ref_lse[live])) <= LSE_TOL_MFMA
+    check_lse(to_np(lse), ref_lse, what=str(case))
 
 
 @pytest.mark.parametrize("key", [11, 14])
@@ -108,7 +105,7 @@ def test_prefill_paged_full_size_sampled(key):
                                         q_pos_offset=L - w.q_len)
         check_close(to_np(o32[s, h][rows]), ref, False, what=f"{w.name} f32 {(s, h)}")
         check_close(to_np(o[s, h][rows]), ref, True, what=f"{w.name} bf16 {(s, h)}")
-        assert np.max(np.abs(to_np(lse[s, h][rows]) - ref_lse)) <= LSE_TOL_MFMA
+        check_lse(to_np(lse[s, h][rows]), ref_lse)
     say(f"{w.name}: sampled rows match")
 
 
@@ -132,7 +129,7 @@ def test_cross_paged_full_size_sampled():
         ref, ref_lse = oracle.attention(wl.bf16_to_f64(inp.q[s, h]), k, v, w.scale, "none", rows=qrows)
         check_close(to_np(o32[s, h][qrows]), ref, False, what=f"{w.name} f32 {(s, h, b)}")
         check_close(to_np(o[s, h][qrows]), ref, True, what=f"{w.name} bf16 {(s, h, b)}")
-        assert np.max(np.abs(to_np(lse[s, h][qrows]) - ref_lse)) <= LSE_TOL_MFMA
+        check_lse(to_np(lse[s, h][qrows]), ref_lse)
     say(f"{w.name}: sampled rows match")
 
 
@@ -164,8 +161,8 @@ def test_prefill_and_decode_share_a_16_token_pool():
                                  page_size=16)
     check_close(to_np(o[:, :, -1]), ref, False, what="prefill's last row on the shared pool")
     check_close(to_np(od), ref, True, what="decode on the shared pool")
-    assert np.max(np.abs(to_np(lse[:, :, -1]) - ref_lse)) <= LSE_TOL_MFMA
-    assert np.max(np.abs(to_np(lsed) - ref_lse)) <= LSE_TOL_MFMA
+    check_lse(to_np(lse[:, :, -1]), ref_lse)
+    check_lse(to_np(lsed), ref_lse)
 
 
 def test_paged_prefill_rejects():

@@ -8,16 +8,19 @@
 // K/V byte is read once, so the kernels are built around keeping enough bytes
 // in flight, not around the matrix cores.
 //
-// decode_split: one wave per (sequence, head, range of 64 pages). The page id
-//   is read once per page as a scalar (it is uniform across the wave) and the
-//   page gather is fused into the K/V loads ("the naive gather-then-attend
-//   route wastes bandwidth", Pattern C). Lane l owns key l/4 of a 16-token
-//   page and a quarter of the head dimension, so each (page, head) slice --
-//   4 KB contiguous for d = 128 -- is read with 16-byte loads that together
-//   cover it exactly once. q.k uses v_dot2_f32_bf16 on packed bf16; the online
-//   softmax ("Flash MSA ...", "Understanding Flash MSA Core Mechanics") runs
-//   over two pages per step. Each range writes its un-normalised state
-//   (m, l, acc) to the workspace.
+// decode_split: one wave per (sequence, head, range of 64 pages). The range's
+//   page ids are loaded once, one per lane, and each is picked as a scalar
+//   (it is uniform across the wave); the page gather is fused into the K/V
+//   loads. Pattern C of that page recommends the two-stage route (gather,
+//   then attend) for paged patterns; fusing the gather is this library's
+//   measured departure from it for decode, where a separate gather would
+//   write and read every cached byte once more. Load j of lane l reads the
+//   16 bytes at 1024 j + 16 l of a (page, head) slice -- 4 KB contiguous for
+//   d = 128 -- so the loads cover the slice exactly once, 1 KB per
+//   instruction. q.k uses v_dot2_f32_bf16 on packed bf16; the online softmax
+//   ("Flash MSA ...", "Understanding Flash MSA Core Mechanics") runs over two
+//   pages per step. Each range writes its un-normalised state (m, l, acc) to
+//   the workspace.
 // decode_combine: merges the ranges of a (sequence, head) with the same
 //   rescale algebra: m* = max m_i, l* = sum 2^(m_i - m*) l_i,
 //   O = sum 2^(m_i - m*) acc_i / l*.
