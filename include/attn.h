@@ -218,6 +218,28 @@ attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_p
                               void* stream);
 
 /*
+ * attn_decode_paged_noalloc -- attn_decode_paged with the split path, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). The split ranges'
+ * partial states live in a fixed 16 MiB array of device memory inside the
+ * library (one per GPU, held until the process ends) instead of a caller
+ * workspace; the call itself allocates nothing.
+ *   Arguments and results as attn_decode_paged (without the workspace).
+ *   If attn_decode_paged_workspace_size(S, H, d, max_pages, page_size)
+ *   exceeds 16 MiB (2^24 bytes) the call returns ATTN_ERR_WORKSPACE and
+ *   nothing runs.
+ *   Every call on one GPU uses that GPU's one array: calls whose work can
+ *   overlap on a GPU (different streams, or host threads, without ordering
+ *   between them) race and give unspecified results. Calls ordered on one
+ *   stream are safe; nothing from an earlier call's contents is read.
+ */
+attn_status attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      void* o, int S, int H, int d, int page_size,
+                                      int max_pages, int num_pages, float scale,
+                                      float* lse, void* stream);
+
+/*
  * attn_prefill_paged -- causal prefill over a paged KV cache ("Optimizing
  * Triton kernels ...", Pattern C, its prefix-caching use), with the page
  * gather fused into the attention's tile loads instead of a separate

@@ -419,3 +419,21 @@ def test_binding_checks_every_tensor_argument(case):
     else:
         with pytest.raises(ValueError, match=rf"^{bad} must"):
             call()
+
+
+def test_noalloc_decode_rejects_work_beyond_its_array():
+    """attn_decode_paged_noalloc holds its partial states in a fixed 16 MiB
+    device array: a size whose workspace would exceed it is refused before
+    anything runs (FAKE pointers: nothing is dereferenced)."""
+    lib = _lib.load()
+    big = lib.attn_decode_paged_workspace_size(256, 32, 128, 2048, 16)
+    assert big > (16 << 20)
+    st = lib.attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 32, 128, 16, 2048, 10000, 0.1,
+                                       None, None)
+    assert st == _lib.ATTN_ERR_WORKSPACE
+    assert lib.attn_decode_paged_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 128, 16, 8, 100, 0.1, None,
+                                         None) == _lib.ATTN_ERR_INVALID_ARG
+    assert lib.attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 128, 32, 8, 100, 0.1, None,
+                                         None) == _lib.ATTN_ERR_UNSUPPORTED
+    # the benchmark's decode fits
+    assert lib.attn_decode_paged_workspace_size(64, 32, 128, 512, 16) <= (16 << 20)

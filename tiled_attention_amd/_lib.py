@@ -33,6 +33,8 @@ _PROTOS = {
     "attn_decode_paged_workspace_size": (_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "attn_decode_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_float, _p, _p, _size, _p]),
+    "attn_decode_paged_noalloc": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                           _c_int, _c_float, _p, _p]),
     "attn_prefill_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_int, _c_float, _p, _p]),
     "attn_cross_paged": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -264,6 +266,27 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, scale, worksp
     _check(load().attn_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
                                     _ptr(o), S, H, d, page_size, max_pages, num_pages, float(scale), _ptr(lse),
                                     _ptr(workspace), ws_bytes, _stream(stream)))
+    return o
+
+
+def attn_decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, o, scale, lse=None, stream=None):
+    """attn_decode_paged's split path with the library's fixed device array in
+    place of a workspace (allocates nothing); calls overlapping on one GPU race."""
+    f32, bf16, _, i32 = _dtypes()
+    _require(q.dim() == 3, "q must be [S, H, d]")
+    S, H, d = q.shape
+    _spec(q, "q", q.shape, (bf16,))
+    _spec(o, "o", q.shape, (bf16,))
+    num_pages, page_size = _pool_specs(k_pool, v_pool, H, d, (bf16,))
+    _require(block_table.dim() == 2, "block_table must be [S, max_pages]")
+    max_pages = block_table.shape[1]
+    _spec(block_table, "block_table", (S, max_pages), (i32,))
+    _spec(seq_lens, "seq_lens", (S,), (i32,))
+    _spec(lse, "lse", (S, H), (f32,), optional=True)
+    _dev(q, k_pool, v_pool, block_table, seq_lens, o, lse)
+    _check(load().attn_decode_paged_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                            _ptr(seq_lens), _ptr(o), S, H, d, page_size, max_pages, num_pages,
+                                            float(scale), _ptr(lse), _stream(stream)))
     return o
 
 

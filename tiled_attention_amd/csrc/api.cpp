@@ -220,6 +220,38 @@ attn_status attn_decode_paged(const void* q, const void* k_pool, const void* v_p
   return launched(attn::launch_decode(a, (hipStream_t)stream));
 }
 
+attn_status attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* seq_lens, void* o, int S, int H,
+                                      int d, int page_size, int max_pages, int num_pages, float scale, float* lse,
+                                      void* stream) {
+  if (!q || !o) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
+  if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return ATTN_ERR_INVALID_ARG;
+  attn_status st = check_paged(k_pool, v_pool, block_table, seq_lens, S, H, d, page_size, max_pages, num_pages);
+  if (st != ATTN_OK) return st;
+  // the partial states must fit the library's fixed device array
+  if (attn::decode_workspace_bytes(S, H, d, max_pages, page_size) > attn::kNoAllocScratchBytes)
+    return ATTN_ERR_WORKSPACE;
+  attn::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = nullptr;
+  a.S = S;
+  a.H = H;
+  a.d = d;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.scale = scale;
+  return launched(attn::launch_decode_noalloc(a, (hipStream_t)stream));
+}
+
 // Shared checks of the two paged prefill entry points (16- or 64-token pages).
 static attn_status paged_fwd(const void* q, const void* k_pool, const void* v_pool, const int32_t* table,
                              const int32_t* lens, void* o, int S, int H, int q_len, int d, int page_size,

@@ -68,6 +68,10 @@ size_t decode_workspace_bytes(int S, int H, int d, int max_pages, int page_size)
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// The split-KV decode with its partial states in the library's static device
+// array (kNoAllocScratchBytes per GPU); a.workspace is ignored.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t launch_decode_noalloc(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_fwd_paged(const PagedFwdArgs& a, hipStream_t stream);
 constexpr int kPrefillPageSize = 64;     // one page of one head is one 64-key tile
 constexpr int kPrefillSmallPage = 16;    // the decode's pages: four per tile

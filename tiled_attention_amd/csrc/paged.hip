@@ -26,8 +26,18 @@
 //   O = sum 2^(m_i - m*) acc_i / l*.
 // With no workspace the whole sequence is one range and decode_split writes
 // O directly.
+#include <mutex>
+
 #include "attn_common.h"
 #include "launch.h"
+
+// Device memory of attn_decode_paged_noalloc, for callers that cannot
+// allocate: the split ranges' partial states (m, l, acc) go here instead of a
+// caller workspace. Each GPU holds its own copy for the life of the process;
+// host code must not pass `scratch` itself to a kernel (in host code the name
+// stands for a host-side shadow), only the address hipGetSymbolAddress gives
+// for the current device.
+static __device__ __align__(256) unsigned char scratch[attn::kNoAllocScratchBytes];
 
 namespace attn {
 namespace {
@@ -333,6 +343,39 @@ size_t decode_workspace_bytes(int S, int H, int d, int max_pages, int page_size)
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.page_size == 64) return a.d == 64 ? launch_decode_d<64, 4>(a, stream) : launch_decode_d<128, 4>(a, stream);
   return a.d == 64 ? launch_decode_d<64, 1>(a, stream) : launch_decode_d<128, 1>(a, stream);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+// Device address of this GPU's `scratch`, looked up once per device (with the
+// device current) and kept.
+static hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_decode_noalloc(const DecodeArgs& a_in, hipStream_t stream) {
+  DecodeArgs a = a_in;
+  hipError_t e = scratch_address(&a.workspace);
+  if (e != hipSuccess) return e;
+  // every partial state the combine reads is written earlier in the same
+  // call, so nothing needs clearing between calls
+  return launch_decode(a, stream);
 }
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
