@@ -292,8 +292,14 @@ struct QTile {
   i32x8 P8[2];              // fp8 V: P of two tiles as fp8 bytes, byte k = key 32 hl + k
 
   // offs: the document offsets (p.doc, or a copy of them in LDS that the
-  // ring does not overwrite before the workgroup's next barrier)
-  __device__ __forceinline__ QTile(const Params& p_, unsigned char* smem_, int bh_, int qt, const int32_t* offs)
+  // ring does not overwrite before the workgroup's next barrier).
+  // early (bf16 Q/K and dense K/V only; the ring must be free): Q is loaded
+  // and the tile stream started from inside the set-up, as soon as their
+  // addresses are known, instead of after it. The set-up runs once per Q
+  // tile and takes microseconds of issue time; its memory latency then
+  // overlaps it.
+  __device__ __forceinline__ QTile(const Params& p_, unsigned char* smem_, int bh_, int qt, const int32_t* offs,
+                                   bool early = false)
       : p(p_), smem(smem_) {
     const int tid = threadIdx.x;
     lane = tid & 63;
@@ -310,6 +316,9 @@ struct QTile {
     // never stored: it stays finite and takes no extra slow-path steps
     qsrc = min(qrow, N - 1);
     head = (size_t)bh * N;
+    if constexpr (!FP8 && !PG) {
+      if (early) load_q();
+    }
 
     const int wr0 = min(wrow0, N - 1), wr1 = min(wrow0 + 31, N - 1);
     RowSpans sp;
@@ -358,16 +367,8 @@ struct QTile {
     // for causal masks) let it restructure the tile loop of the fp8 kernels
     // in a way that overflows the VGPRs
     asm volatile("" : "+s"(t_lo), "+s"(NK));
-    klo_m1 = sp.lane.lo - 1;
-    khi = sp.lane.hi;
-    // FULL range of this wave's 32 rows (a contiguous run of tiles), local indices
-    full_tiles(sp.wave_first, sp.wave_last, BN, &f_lo, &f_hi);
-    f_lo = min(max(f_lo - t_lo, 0), NK);
-    f_hi = min(max(f_hi - t_lo, f_lo), NK);
-    qscale = 1.f;
-    if constexpr (FP8) qscale = p.q_scale[bh * p.nsb + m0 / 128];
 
-    // ---- per-lane offsets (loop invariant)
+    // ---- the tile stream: DMA offsets, LDS slots, K/V descriptors
 #pragma unroll
     for (int u = 0; u < KLD; ++u) {
       const int off = (u * NW + wave) * 1024 + lane * 16;
@@ -383,6 +384,33 @@ struct QTile {
       else
         vdma[u] = row * VROW + 16 * (ch ^ swz_v<VROW>(row));
     }
+    const uint32_t lds0 = lds_addr(smem);
+    lds_k = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
+    lds_v = __builtin_amdgcn_readfirstlane(lds0 + NS * C::K_SLOT + wave * 1024);
+    const uint64_t kb = PG ? 0 : (uint64_t)(uintptr_t)p.k + (head + (size_t)t_lo * BN) * KROW;
+    const uint64_t vb = PG ? 0 : (uint64_t)(uintptr_t)p.v + (head + (size_t)t_lo * BN) * VROW;
+    const int rem = __builtin_amdgcn_readfirstlane(N - t_lo * BN);
+    ks.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kb >> 32)) << 32) |
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kb);
+    vs.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(vb >> 32)) << 32) |
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)vb);
+    ks.remain = (int64_t)rem * KROW;
+    vs.remain = (int64_t)rem * VROW;
+
+    if constexpr (!FP8 && !PG) {
+      if (early) start_stream();
+    }
+
+    // ---- per-lane state of the loop
+    klo_m1 = sp.lane.lo - 1;
+    khi = sp.lane.hi;
+    // FULL range of this wave's 32 rows (a contiguous run of tiles), local indices
+    full_tiles(sp.wave_first, sp.wave_last, BN, &f_lo, &f_hi);
+    f_lo = min(max(f_lo - t_lo, 0), NK);
+    f_hi = min(max(f_hi - t_lo, f_lo), NK);
+    qscale = 1.f;
+    if constexpr (FP8) qscale = p.q_scale[bh * p.nsb + m0 / 128];
+
     // K read of k-step t: lane l32 supplies S^T row l32 of block 0 (block 1:
     // kBlock1Rows further, same swizzle), chunk of half hl. With fp8 V the
     // rows are permuted so that lane (row l32, half hl) ends up holding keys
@@ -423,24 +451,11 @@ struct QTile {
         vread[e] = (4 * hl + rr) * VROW + 16 * ((4 * e + 2 * (g & 1) + (cc >> 1)) ^ sv) + 8 * (cc & 1);
     }
 
-    const uint32_t lds0 = lds_addr(smem);
-    lds_k = __builtin_amdgcn_readfirstlane(lds0 + wave * 1024);
-    lds_v = __builtin_amdgcn_readfirstlane(lds0 + NS * C::K_SLOT + wave * 1024);
-    const uint64_t kb = PG ? 0 : (uint64_t)(uintptr_t)p.k + (head + (size_t)t_lo * BN) * KROW;
-    const uint64_t vb = PG ? 0 : (uint64_t)(uintptr_t)p.v + (head + (size_t)t_lo * BN) * VROW;
-    const int rem = __builtin_amdgcn_readfirstlane(N - t_lo * BN);
-    ks.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kb >> 32)) << 32) |
-              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kb);
-    vs.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(vb >> 32)) << 32) |
-              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)vb);
-    ks.remain = (int64_t)rem * KROW;
-    vs.remain = (int64_t)rem * VROW;
-
     m_ref = -INFINITY;
     m_use = 0.f;
     limit = -1.f;
     c_next = tile_scale(0);
-    vq0 = 127;                // the tile before the first: P is 0 there
+    vq0 = 127;                // the tile before the first (no P V there)
     vq1 = v_exponent(0);
     l_run = 0.f;
   }
@@ -570,7 +585,7 @@ struct QTile {
     vs.base += BN * VROW;
     vs.remain -= BN * VROW;
   }
-  // zeros into V slot SLOT (the V of the tile before the first)
+  // zero-size loads into V slot SLOT (the V of the tile before the first)
   template <int SLOT>
   __device__ __forceinline__ void issue_v_zero() {
     const i32x4 rs = {(int)(uint32_t)vs.base, (int)(uint32_t)(vs.base >> 32), 0, kBufferFlags};
@@ -716,6 +731,19 @@ struct QTile {
     return e[0];
   }
 
+  // First tile of the Q tile: the reference is the exact row max of its
+  // scores (none yet: a row that sees no key here keeps -inf, so its next
+  // tile takes the slow path). Nothing is rescaled: l and acc are still 0.
+  template <int B>
+  __device__ __forceinline__ void set_reference(float c) {
+    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mq[r & 3] = max3(mq[r & 3], S[B][0][r], S[B][1][r]);
+    m_ref = half_swap_max(max3(mq[0], mq[1], fmaxf(mq[2], mq[3]))) * c;
+    m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    limit = m_ref == -INFINITY ? -1.f : kLimit;
+  }
+
   // Slow path for tile i in S[B]/P[B]: the reference becomes the exact row max
   // (if it rises), P is recomputed against it, and l and acc (which holds P V
   // of the tiles before i) are rescaled.
@@ -741,7 +769,9 @@ struct QTile {
 
   // One pipeline step at local tile i (PH = i mod U): S of tile i+1 and P V of
   // tile i-1 on the matrix cores, the exponentials of tile i on the VALU.
-  template <int PH>
+  // FIRST (i = 0): there is no P V yet, and the row max of the tile sets the
+  // reference before the exponentials, which are then formed once.
+  template <int PH, bool FIRST = false>
   __device__ __forceinline__ void step(int i) {
     constexpr int B = PH & 1;          // S[B] holds S_i, P[B] receives P_i
     constexpr int BO = B ^ 1;          // S[BO] receives S_{i+1}, P[BO] holds P_{i-1}
@@ -771,13 +801,16 @@ struct QTile {
     // unconditional, so the block has no branch: for i + 1 == NK the slot
     // holds a tile past the band whose scores are never used
     qk<(PH + 1) % NS, BO>();
-    pv<(PH + NS - 1) % NS, BO>(vpv);
+    if constexpr (!FIRST) pv<(PH + NS - 1) % NS, BO>(vpv);
+    if constexpr (FIRST) set_reference<B>(c);
     float psum = exponentials<B>(c, m_exp());
     // issue order: every LDS operand read of the step first, then each MFMA
     // followed by a run of the softmax VALU work
-    __builtin_amdgcn_sched_group_barrier(0x100, kStepReads, 0);
+    constexpr int kReads = FIRST ? 2 * QK_STEPS * (FP8 ? 2 : 1) : kStepReads;
+    constexpr int kMfma = FIRST ? 2 * QK_STEPS : kStepMfma;
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
-    for (int k = 0; k < kStepMfma; ++k) {
+    for (int k = 0; k < kMfma; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
@@ -792,7 +825,9 @@ struct QTile {
     }
     // a lane without a reference yet, or a tile sum past the limit, moves it
     // (before P V of the tile, which the next step issues)
-    if (__builtin_expect(__any(!(psum <= limit)), 0)) rebase<B>(c, psum);
+    if constexpr (!FIRST) {
+      if (__builtin_expect(__any(!(psum <= limit)), 0)) rebase<B>(c, psum);
+    }
     // the sum of P itself (fp8 P: the sum of the scaled values times 2^-3)
     l_run += V8 ? psum * (1.f / (1 << kPShiftFp8)) : psum;
     if constexpr (!kEarlyRefill) refill<PH>();
@@ -808,6 +843,11 @@ struct QTile {
   template <int PH>
   __device__ __forceinline__ void step_if(int i) {
     if (i < NK) step<PH>(i);
+  }
+  // steps 1 .. U-1 (the first group after step 0)
+  template <int... PHS>
+  __device__ __forceinline__ void run_head(std::integer_sequence<int, PHS...>) {
+    (step_if<PHS + 1>(PHS + 1), ...);
   }
 
   // P V of the last tile (local NK - 1, phase PH)
@@ -829,7 +869,9 @@ struct QTile {
   __device__ __forceinline__ void run_drain(int ph, std::integer_sequence<int, PHS...>) {
     ((ph == PHS ? drain<PHS>() : (void)0), ...);
   }
-  // batch {K_{x+NS}, V_{x+NS-2}} of step x = XS + 1 - NS; V_{-1} is zeros
+  // batch {K_{x+NS}, V_{x+NS-2}} of step x = XS + 1 - NS. V_{-1} is never
+  // read (step 0 has no P V); its zero-size loads keep every batch at the
+  // same count of loads, which the waits rely on
   template <int XS>
   __device__ __forceinline__ void prologue_batch() {
     issue_k<XS + 1>();
@@ -860,12 +902,13 @@ struct QTile {
     // later prologue batches are outstanding (the counter drains in order);
     // those batches keep streaming under the first steps
     q_landed<(NS - 1) * L>();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) P[1][q] = (bf16x8){};
-    P8[1] = (i32x8){};
-    if (NK > 0) qk<0, 0>();
+    if (NK > 0) {
+      qk<0, 0>();
+      step<0, true>(0);
+    }
+    run_head(std::make_integer_sequence<int, U - 1>{});
 
-    int i = 0;
+    int i = U;
     for (; i + U <= NK; i += U) run_steps(i, std::make_integer_sequence<int, U>{});
     run_tail(i, std::make_integer_sequence<int, U - 1>{});
     if (NK > 0) run_drain((NK - 1) % U, std::make_integer_sequence<int, U>{});
@@ -1014,17 +1057,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // searched there (a search in global memory costs several dependent
     // round trips per workgroup); a barrier then frees the LDS for the ring
     const bool lds_offs = p.order == ORDER_DOC;
-    QTile<D, FP8, OUT_F32, PG, V8> a(p, smem, bh, tb, lds_offs ? (const int32_t*)(smem + 2 * NT * sizeof(int)) : p.doc);
-    a.load_q();
-    if (lds_offs) __syncthreads();
-    a.start_stream();
+    const bool early = !FP8 && !PG && !lds_offs;
+    QTile<D, FP8, OUT_F32, PG, V8> a(p, smem, bh, tb, lds_offs ? (const int32_t*)(smem + 2 * NT * sizeof(int)) : p.doc,
+                                     early);
+    if (!early) {
+      a.load_q();
+      if (lds_offs) __syncthreads();
+      a.start_stream();
+    }
     a.loop();
     a.epilogue();
   }
   if (p.pair && ta != tb) {
-    QTile<D, FP8, OUT_F32, PG, V8> b(p, smem, bh, ta, p.doc);
-    b.load_q();
-    b.start_stream();
+    // the first tile's loop ended with every wave past its last LDS read
+    QTile<D, FP8, OUT_F32, PG, V8> b(p, smem, bh, ta, p.doc, !FP8 && !PG);
+    if (FP8 || PG) {
+      b.load_q();
+      b.start_stream();
+    }
     b.loop();
     b.epilogue();
   }
