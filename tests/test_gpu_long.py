@@ -96,7 +96,7 @@ def test_long_decode(page):
     ref, ref_lse = oracle.decode(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
                                  inp.block_table.numpy(), inp.seq_lens.numpy(), 1.0 / math.sqrt(d), page_size=page)
     check_close(to_np(o), ref, True, what=f"decode L={L} page={page}")
-    check_lse(to_np(lse), ref_lse, tol=1e-3)
+    check_lse(to_np(lse), ref_lse)
 
 
 def test_head_of_more_than_2gib_of_bytes():

@@ -49,7 +49,7 @@ def test_decode_small_elementwise(d, use_ws, lens, page):
     o, lse = _decode(inp, scale, use_ws)
     ref, ref_lse = _oracle_decode(inp, scale)
     check_close(to_np(o), ref, True, what=f"decode d={d}")
-    check_lse(to_np(lse), ref_lse, tol=1e-3)
+    check_lse(to_np(lse), ref_lse)
 
 
 def test_decode_exact_page_multiples_and_single_token():
@@ -105,7 +105,7 @@ def test_workload_4_full_size(key):
     ref, ref_lse = _oracle_decode(inp, w.scale)
     err = check_close(to_np(o), ref, True, what=w.name)
     err1 = check_close(to_np(o_direct), ref, True, what=w.name + " (one pass)")
-    check_lse(to_np(lse), ref_lse, tol=1e-3)
+    check_lse(to_np(lse), ref_lse)
     say(f"{w.name}: max abs err {err:.3g} (split), {err1:.3g} (one pass)")
 
     # bit-exact gather of every sequence against the oracle's gather

@@ -175,3 +175,33 @@ def test_paged_prefill_rejects():
         A.attn_prefill_paged(q, pool32, pool32, table, lens, o, 0.125)
     torch.cuda.synchronize()
     assert torch.all(o == 3.0)
+
+
+@pytest.mark.parametrize("page", [64, 16])
+def test_two_stage_route_equals_fused(page):
+    """The two-stage route of "Optimizing Triton kernels ...", Pattern C --
+    gather every sequence's pages into a dense copy, then attend over it --
+    gives the fused kernel's output bit for bit: both visit the same keys in
+    the same 64-key tiles, one reading pages, the other the copy (read as
+    contiguous 64-token pages through an identity table). Rows of the copy
+    past each sequence's length are NaN-poisoned and never read."""
+    import bench
+    S, H, q_len, d = 3, 4, 300, 128
+    inp = wl.paged_inputs(S, H, d, 300, 1500, seed=77 + page, page_size=page, spare=5, q_rows=q_len,
+                          max_pages=1536 // page)
+    scale = 1.0 / math.sqrt(d)
+    kp, vp, bt, lens = inp.k_pool.cuda(), inp.v_pool.cuda(), inp.block_table.cuda(), inp.seq_lens.cuda()
+    q = inp.q.cuda()
+    fused = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    A.attn_prefill_paged(q, kp, vp, bt, lens, fused, scale)
+    T = bt.shape[1] * page
+    assert T % 64 == 0                     # table rows of 1536 tokens: 24 pages of 64 or 96 of 16
+    k_out = torch.full((S, H, T, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v_out = torch.full_like(k_out, float("nan"))
+    A.attn_gather_paged(kp, vp, bt, lens, k_out, v_out)
+    two = bench.two_stage_views(q, k_out, v_out, lens, H)
+    o2 = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    A.attn_prefill_paged(two["q"], two["k"], two["v"], two["table"], two["lens"], o2.view(two["q"].shape), scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(fused.float()).all()
+    assert torch.equal(o2.view(torch.int16), fused.view(torch.int16))

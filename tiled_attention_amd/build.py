@@ -63,6 +63,31 @@ def build(verbose=False, extra_flags=()):
     return LIB
 
 
+def resource_usage(src):
+    """Per-kernel register, scratch and spill figures of one source, from the
+    compiler's kernel-resource-usage remarks (a compile to a throw-away
+    object). Returns {kernel name: {field: int}}."""
+    import re
+    import tempfile
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [_hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", os.path.join(tmp, "x.o")] + \
+            COMMON_FLAGS + ["-Rpass-analysis=kernel-resource-usage"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")
+    out, cur = {}, None
+    for line in res.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            out[cur] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^]]*\])?: (\d+)", line)
+        if m and cur is not None:
+            out[cur][m.group(1).strip()] = int(m.group(2))
+    return out
+
+
 if __name__ == "__main__":
     flags = [a for a in sys.argv[1:] if a != "-v"]
     print(build(verbose="-v" in sys.argv, extra_flags=flags))
