@@ -88,6 +88,20 @@ def resource_usage(src):
     return out
 
 
+def assembly(src):
+    """The gfx950 assembly the compiler writes for one source (a throw-away
+    compile with -S)."""
+    import tempfile
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "x.s")
+        cmd = [_hipcc(), "-x", "hip", "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", out] + COMMON_FLAGS
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed for {src}:\n{res.stderr}")
+        with open(out) as f:
+            return f.read()
+
+
 if __name__ == "__main__":
     flags = [a for a in sys.argv[1:] if a != "-v"]
     print(build(verbose="-v" in sys.argv, extra_flags=flags))

@@ -204,14 +204,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // 16 bytes per lane from buffer offset voff to LDS at m0 + lane * 16. The
 // compiler does not see this load: its completion is waited for explicitly
-// (sync_tiles). The s_nop covers the SALU-writes-M0 -> LDS DMA hazard. No
-// memory clobber: the slot written is one no wave reads until a later
-// sync_tiles (whose clobber orders the LDS reads), and volatile asm keeps its
-// place after the sync_tiles that freed the slot.
+// (sync_tiles). The s_nop covers the SALU-writes-M0 -> LDS DMA hazard; M0 is
+// declared clobbered. No memory clobber: the slot written is one no wave
+// reads until a later sync_tiles (whose clobber orders the LDS reads), and
+// volatile asm keeps its place after the sync_tiles that freed the slot.
 __device__ __forceinline__ void dma16(uint32_t m0v, int voff, i32x4 rsrc) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(m0v), "v"(voff), "s"(rsrc));
+               : "s"(m0v), "v"(voff), "s"(rsrc)
+               : "m0");
 }
 
 // Wait until at most N of this wave's loads are outstanding, then barrier.
@@ -225,14 +226,24 @@ __device__ __forceinline__ void sync_tiles() {
 // A stream of K (or V) tiles of one head through its LDS ring: a raw buffer
 // descriptor whose base walks one tile per issue and whose size is clipped at
 // the end of the sequence (so rows >= N load as zeros).
+template <int ROWB>
 struct TileStream {
   uint64_t base;    // global address of the next tile to issue
-  int64_t remain;   // bytes from base to the end of the head (may go <= 0; a head
-                    // can hold 2^31 or more bytes)
-  // The size field is 32 bits: past 2^31 - 1 it is clamped, which loses
-  // nothing, since one issue reads at most one tile (< 2^31 bytes) past base.
+  int rows;         // rows from base to the end of the head (may go <= 0)
+  // The descriptor's size field is 32 bits and a head can hold 2^31 bytes or
+  // more: the row count is clamped first, which loses nothing, since one
+  // issue reads one tile (BN rows) past base. Scalar 32-bit operations only.
   __device__ __forceinline__ i32x4 rsrc() const {
-    const int n = remain <= 0 ? 0 : remain >= 0x7fffffff ? 0x7fffffff : (int)remain;
+    constexpr int kMaxRows = 0x7fffffff / ROWB;
+    // scalar instructions, so the descriptor stays in SGPRs (the compiler
+    // would fold min and max into a vector med3). s_max / s_min write SCC,
+    // which the compiler may hold live across this statement (the carry of a
+    // 64-bit address add split around it): it is declared clobbered.
+    int n;
+    asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2\n\ts_mul_i32 %0, %0, %3"
+        : "=&s"(n)
+        : "s"(rows), "i"(kMaxRows), "i"(ROWB)
+        : "scc");
     return (i32x4){(int)(uint32_t)base, (int)(uint32_t)(base >> 32), n, kBufferFlags};
   }
 };
@@ -274,7 +285,8 @@ struct QTile {
   int kread[QK_STEPS * (FP8 ? 2 : 1)];
   int vread[DE];
   uint32_t lds_k, lds_v;    // this wave's DMA destinations in slot 0 (K, V)
-  TileStream ks, vs;
+  TileStream<KROW> ks;
+  TileStream<VROW> vs;
   // paged mode: pools, page ids in LDS, valid keys of the list, next tile of each stream
   uint64_t pool_k, pool_v;
   const int* pg_ids;
@@ -394,8 +406,8 @@ struct QTile {
               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kb);
     vs.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(vb >> 32)) << 32) |
               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)vb);
-    ks.remain = (int64_t)rem * KROW;
-    vs.remain = (int64_t)rem * VROW;
+    ks.rows = rem;
+    vs.rows = rem;
 
     if constexpr (!FP8 && !PG) {
       if (early) start_stream();
@@ -566,7 +578,7 @@ struct QTile {
 #pragma unroll
     for (int u = 0; u < KLD; ++u) dma16(lds_k + SLOT * C::K_SLOT + u * NW * 1024, kdma[u], rs);
     ks.base += BN * KROW;
-    ks.remain -= BN * KROW;
+    ks.rows -= BN;
   }
   template <int SLOT>
   __device__ __forceinline__ void issue_v() {
@@ -583,7 +595,7 @@ struct QTile {
 #pragma unroll
     for (int u = 0; u < VLD; ++u) dma16(lds_v + SLOT * C::V_SLOT + u * NW * 1024, vdma[u], rs);
     vs.base += BN * VROW;
-    vs.remain -= BN * VROW;
+    vs.rows -= BN;
   }
   // zero-size loads into V slot SLOT (the V of the tile before the first)
   template <int SLOT>
