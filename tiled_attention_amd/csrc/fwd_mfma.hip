@@ -98,11 +98,14 @@ struct Cfg {
   static constexpr int V_SLOT = BN * VROW;
   static constexpr int KLD = K_SLOT / (16 * NT);  // DMA loads per thread per K tile
   static constexpr int VLD = V_SLOT / (16 * NT);
-  // LDS ring slots (K and V alike): the deepest ring that still lets two
-  // workgroups share a CU's 160 KB.
-  static constexpr int NS = (4 * (K_SLOT + V_SLOT) <= 80 * 1024) ? 4 : (3 * (K_SLOT + V_SLOT) <= 80 * 1024) ? 3 : 2;
+  // LDS ring slots (K and V alike): four for bf16 d = 64 (half of a CU's
+  // 160 KB per workgroup, two workgroups per CU), two otherwise. Measured
+  // with the mask-free loop: a 3-slot fp8 ring (a 6-step unroll) spilled
+  // VGPRs and ran 3% slower than two slots on the all-fp8 kernel; at d = 64
+  // four slots are 1% faster than two.
+  static constexpr int NS = (!FP8 && 4 * (K_SLOT + V_SLOT) <= 80 * 1024) ? 4 : 2;
   // main-loop unroll: a multiple of NS (compile-time slots) and of 2 (the S / P double buffers)
-  static constexpr int U = NS == 3 ? 6 : NS;
+  static constexpr int U = NS;
   static constexpr int LDS = NS * (K_SLOT + V_SLOT);
   static constexpr int QK_STEPS = FP8 ? D / 64 : D / 16;
   static constexpr int DE = D / 32;             // 32-row blocks of O^T
@@ -783,7 +786,9 @@ struct QTile {
   // tile i-1 on the matrix cores, the exponentials of tile i on the VALU.
   // FIRST (i = 0): there is no P V yet, and the row max of the tile sets the
   // reference before the exponentials, which are then formed once.
-  template <int PH, bool FIRST = false>
+  // MASK: the step tests whether tile i is outside this wave's FULL range and
+  // masks it then; the loop's bulk runs without (see loop()).
+  template <int PH, bool FIRST = false, bool MASK = true>
   __device__ __forceinline__ void step(int i) {
     constexpr int B = PH & 1;          // S[B] holds S_i, P[B] receives P_i
     constexpr int BO = B ^ 1;          // S[BO] receives S_{i+1}, P[BO] holds P_{i-1}
@@ -803,13 +808,15 @@ struct QTile {
         vq1 = v_exponent(i + 1);
       }
     }
-    // refill the slots freed at this step's sync_tiles. A ring of 2 or 3
-    // slots is refilled at once, so the tiles have a whole step to land
+    // refill the slots freed at this step's sync_tiles. A ring of 2 slots
+    // is refilled at once, so the tiles have a whole step to land
     // before the next step waits for them; a 4-slot ring has slack to spare
     // and refills after the MFMA block, where a stall on the texture-address
     // queue overlaps the MFMAs in flight.
     if constexpr (kEarlyRefill) refill<PH>();
-    if ((unsigned)(i - f_lo) >= (unsigned)(f_hi - f_lo)) mask<B>(i);
+    if constexpr (MASK) {
+      if ((unsigned)(i - f_lo) >= (unsigned)(f_hi - f_lo)) mask<B>(i);
+    }
     // unconditional, so the block has no branch: for i + 1 == NK the slot
     // holds a tile past the band whose scores are never used
     qk<(PH + 1) % NS, BO>();
@@ -845,7 +852,7 @@ struct QTile {
     if constexpr (!kEarlyRefill) refill<PH>();
   }
 
-  static constexpr bool kEarlyRefill = NS <= 3;
+  static constexpr bool kEarlyRefill = NS == 2;
   template <int PH>
   __device__ __forceinline__ void refill() {
     issue_k<PH % NS>();                // K_{i+NS} into K_i's slot
@@ -872,6 +879,10 @@ struct QTile {
   template <int... PHS>
   __device__ __forceinline__ void run_steps(int i, std::integer_sequence<int, PHS...>) {
     (step<PHS>(i + PHS), ...);
+  }
+  template <int... PHS>
+  __device__ __forceinline__ void run_steps_full(int i, std::integer_sequence<int, PHS...>) {
+    (step<PHS, false, false>(i + PHS), ...);
   }
   template <int... PHS>
   __device__ __forceinline__ void run_tail(int i, std::integer_sequence<int, PHS...>) {
@@ -920,7 +931,15 @@ struct QTile {
     }
     run_head(std::make_integer_sequence<int, U - 1>{});
 
+    // The bulk: tiles every row of this wave sees in full, in a loop with no
+    // mask code. A conditional mask inside the step made the compiler move
+    // the 32 scores between registers at the join on every step (measured
+    // 3-4% of the causal d = 64 launch); the tiles around the bulk go through
+    // steps that test for the mask. Waves may split their steps differently:
+    // each still runs one barrier per step.
     int i = U;
+    const int bulk_end = f_lo <= U ? f_hi : U;
+    for (; i + U <= bulk_end; i += U) run_steps_full(i, std::make_integer_sequence<int, U>{});
     for (; i + U <= NK; i += U) run_steps(i, std::make_integer_sequence<int, U>{});
     run_tail(i, std::make_integer_sequence<int, U - 1>{});
     if (NK > 0) run_drain((NK - 1) % U, std::make_integer_sequence<int, U>{});
