@@ -25,7 +25,8 @@
 //    LDS DMA (buffer_load_dwordx4 ... lds) NS-1 tiles ahead of use. The main
 //    loop is unrolled so that every slot is a compile-time LDS offset, and the
 //    buffer descriptors advance by one tile per step with scalar adds; a
-//    descriptor clipped at the end of the sequence reads rows past N as zeros.
+//    descriptor clipped at the Q tile's last key tile (or the end of the
+//    sequence) reads the rows past it as zeros, with no memory traffic.
 //    Rows are stored unpadded with the 16-byte chunks XOR-swizzled by row, so
 //    the 16-byte K reads and the transposed V reads hit distinct banks.
 //  * Software pipeline: while the VALU computes the exponentials of tile i,
@@ -228,7 +229,7 @@ __device__ __forceinline__ void sync_tiles() {
 
 // A stream of K (or V) tiles of one head through its LDS ring: a raw buffer
 // descriptor whose base walks one tile per issue and whose size is clipped at
-// the end of the sequence (so rows >= N load as zeros).
+// the Q tile's last key tile or the sequence (rows past it load as zeros).
 template <int ROWB>
 struct TileStream {
   uint64_t base;    // global address of the next tile to issue
@@ -404,7 +405,9 @@ struct QTile {
     lds_v = __builtin_amdgcn_readfirstlane(lds0 + NS * C::K_SLOT + wave * 1024);
     const uint64_t kb = PG ? 0 : (uint64_t)(uintptr_t)p.k + (head + (size_t)t_lo * BN) * KROW;
     const uint64_t vb = PG ? 0 : (uint64_t)(uintptr_t)p.v + (head + (size_t)t_lo * BN) * VROW;
-    const int rem = __builtin_amdgcn_readfirstlane(N - t_lo * BN);
+    // the streams end with the Q tile's last tile (or the head): the ring's
+    // refills past it (NS - 1 K tiles, NS - 2 V tiles) then read nothing
+    const int rem = __builtin_amdgcn_readfirstlane(min(N - t_lo * BN, NK * BN));
     ks.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kb >> 32)) << 32) |
               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kb);
     vs.base = ((uint64_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(vb >> 32)) << 32) |
@@ -818,7 +821,7 @@ struct QTile {
       if ((unsigned)(i - f_lo) >= (unsigned)(f_hi - f_lo)) mask<B>(i);
     }
     // unconditional, so the block has no branch: for i + 1 == NK the slot
-    // holds a tile past the band whose scores are never used
+    // holds zeros (the stream ends at tile NK - 1) whose scores are never used
     qk<(PH + 1) % NS, BO>();
     if constexpr (!FIRST) pv<(PH + NS - 1) % NS, BO>(vpv);
     if constexpr (FIRST) set_reference<B>(c);
