@@ -446,17 +446,18 @@ def traffic_for(digest):
 
 
 def clock_for(digest):
-    """Shader clock (GHz) measured for the main kernel under load: GPU-busy
-    cycles (GRBM_GUI_ACTIVE) over dispatch time, from a committed counter
-    pass; None once the kernel source has changed."""
+    """Shader clock (GHz) of the main kernel under load, as (lower, upper)
+    bounds from a committed counter pass: busy cycles per shader engine over
+    the dispatch time, and the counting window's cycles per XCD over the
+    dispatch time. None once the kernel source has changed."""
     try:
         with open(CLOCK_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_digest") != digest:
+    if t.get("kernel_source_digest") != digest or "clock_ghz" not in t:
         return None
-    return t.get("clock_ghz")
+    return t["clock_ghz"], t.get("clock_ghz_upper", t["clock_ghz"])
 
 
 def wl_keys():
@@ -579,9 +580,10 @@ def main():
             "algorithmic_flops_per_launch": wk.flops, "kernel_source_digest": digest}
     ghz = clock_for(digest) if main_key == 2 else None
     if ghz:
-        # the same rate against the peak at the clock the kernel ran at
-        roof["clock_ghz_measured"] = ghz
-        roof["frac_at_measured_clock"] = round(achieved / (peak * ghz / 2.4), 4)
+        # the same rate against the peak scaled to the clock the kernel ran at
+        # (between the two bounds; the lower one is close)
+        roof["clock_ghz_measured"] = list(ghz)
+        roof["frac_at_measured_clock"] = [round(achieved / (peak * g / 2.4), 4) for g in ghz]
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
