@@ -158,14 +158,17 @@ __device__ inline int doc_index(int count, int nd) {
 //   lane: this lane's row.
 // Every row argument is < N; all but `row` are uniform across the wave.
 struct RowSpans {
-  KeySpan lane, wave_first, wave_last, tile_first, tile_last;
+  KeySpan lane, lane2, wave_first, wave_last, tile_first, tile_last;
 };
 
+// Spans of a workgroup's first and last rows, of a wave's first and last
+// rows, and of the lane's rows `row` and `row2` (both inside the wave's rows).
 __device__ inline RowSpans row_spans(int mask, int window, const int32_t* offs, int nd, int N, int tile_r0,
-                                     int tile_r1, int wave_r0, int wave_r1, int row) {
+                                     int tile_r1, int wave_r0, int wave_r1, int row, int row2) {
   RowSpans r;
   if (!is_document(mask)) {
     r.lane = band_span(mask, window, N, row);
+    r.lane2 = band_span(mask, window, N, row2);
     r.wave_first = band_span(mask, window, N, wave_r0);
     r.wave_last = band_span(mask, window, N, wave_r1);
     r.tile_first = band_span(mask, window, N, tile_r0);
@@ -185,13 +188,23 @@ __device__ inline RowSpans row_spans(int mask, int window, const int32_t* offs, 
   r.wave_first = doc_span(causal, offs[d], offs[d + 1], N, wave_r0);
   d = doc_index(cw1, nd);
   r.wave_last = doc_span(causal, offs[d], offs[d + 1], N, wave_r1);
-  // this lane's row: the document starts between the wave's first and last
-  // rows (usually none or one) decide it
-  int c = cw0;
-  for (int t = cw0; t < cw1; ++t) c += offs[t] <= row ? 1 : 0;
+  // the lane's rows: the document starts between the wave's first and last
+  // rows (usually none or one) decide them
+  int c = cw0, c2 = cw0;
+  for (int t = cw0; t < cw1; ++t) {
+    c += offs[t] <= row ? 1 : 0;
+    c2 += offs[t] <= row2 ? 1 : 0;
+  }
   d = doc_index(c, nd);
   r.lane = doc_span(causal, offs[d], offs[d + 1], N, row);
+  d = doc_index(c2, nd);
+  r.lane2 = doc_span(causal, offs[d], offs[d + 1], N, row2);
   return r;
+}
+
+__device__ inline RowSpans row_spans(int mask, int window, const int32_t* offs, int nd, int N, int tile_r0,
+                                     int tile_r1, int wave_r0, int wave_r1, int row) {
+  return row_spans(mask, window, offs, nd, N, tile_r0, tile_r1, wave_r0, wave_r1, row, row);
 }
 
 // Workgroup id -> work unit, so that consecutive units land on one XCD.

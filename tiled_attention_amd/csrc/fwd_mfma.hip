@@ -9,7 +9,8 @@
 // -- the product of the two blocks' scales multiplies the fp8 dot products; it
 // is folded into the exponent's scale factor.
 //
-// Mapping onto CDNA4 (a workgroup is 4 waves = 128 query rows, 32 per wave):
+// Mapping onto CDNA4 (a workgroup is 4 waves = 128 query rows, 32 per wave;
+// bf16 d = 64 dense: 64 rows and one 32-key half of every tile per wave, below):
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x64_f8f6f4 for
 //    fp8): K is the A operand, read from LDS; Q is the B operand, held in
 //    VGPRs for the whole K loop. In the 32x32 result lane l owns query row
@@ -33,6 +34,16 @@
 //    the matrix cores run S = K Q^T of tile i+1 and O += P V of tile i-1 (P V
 //    is one tile behind, so neither depends on the softmax in flight), in one
 //    interleaved block.
+//  * bf16 d = 64, dense K/V, from 4096 keys (key split): wave w takes rows
+//    64 (w & 1) .. +63 as two 32-row blocks and keys 32 (w >> 1) .. +31 of
+//    every tile, so each K / V operand read from LDS feeds two MFMAs (one per
+//    row block): half the LDS reads per MFMA, at the same MFMA and softmax
+//    work per step. The scores fit in one buffer per row block (the step runs
+//    in three phases, each block's scores overwritten after their use). The
+//    two waves that share rows keep separate references and sums over their
+//    key halves; the epilogue merges them through LDS, each wave finishing
+//    one row block. That merge is a per-Q-tile cost: below 4096 keys the
+//    32-row layout is as fast or faster.
 //  * Reference without a per-tile max: P = 2^(S*c - m) against a reference m
 //    that is the exact row max when it is set. A tile whose sum of P stays
 //    below 2^24 per lane keeps it (no overflow is possible in fp32 / bf16 and
@@ -178,6 +189,7 @@ enum UnitOrder {
   ORDER_TILES = 3    // one Q tile per unit, tile-major from the last tile down (costs never fall with
                      // the tile index for these masks), heads innermost so a head stays on one XCD
 };
+constexpr int kKeySplitMinN = 4096;   // bf16 d = 64: the key-split layout from this length
 constexpr int kOrderMaxDocs = 8192;  // document offsets staged in LDS for the costing (and the LDS
                                      // must hold them behind the 2 NT ints of costs and ranks)
 
@@ -252,17 +264,24 @@ struct TileStream {
   }
 };
 
-template <int D, bool FP8, bool OUT_F32, int PG, bool V8>
+template <int D, bool FP8, bool OUT_F32, int PG, bool V8, bool KSPLIT>
 struct QTile {
   static_assert(!(PG && FP8), "paged K/V is bf16");
   static_assert(!V8 || FP8, "fp8 V comes with fp8 Q and K");
   using C = Cfg<D, FP8, V8>;
   static constexpr int KROW = C::KROW, VROW = C::VROW, QK_STEPS = C::QK_STEPS, DE = C::DE;
   static constexpr int KLD = C::KLD, VLD = C::VLD, L = KLD + VLD, NS = C::NS, U = C::U;
-  // per step: LDS operand reads and MFMAs
-  static constexpr int kStepReads = 2 * QK_STEPS * (FP8 ? 2 : 1) + (V8 ? 4 : 8) * DE;
-  static constexpr int kStepMfma = 2 * QK_STEPS + (V8 ? 1 : 4) * DE;
   static constexpr float kLimit = V8 ? kSumLimitFp8 : kSumLimit;
+  // key split (bf16 d = 64, dense K/V): two 32-row blocks per wave, 32 keys of each tile
+  static constexpr bool KS = KSPLIT;
+  static_assert(!KS || (D == 64 && !FP8 && !PG), "the key split is the bf16 d = 64 dense layout");
+  static constexpr int NJ = KS ? 2 : 1;     // 32-row blocks per wave
+  // LDS bytes of one row block's partial state handed over in the key-split epilogue
+  static constexpr int kXchgBytes = DE * 16 * 64 * 4 + 64 * 8;
+  // per step: LDS operand reads and MFMAs
+  static constexpr int kStepReads = KS ? QK_STEPS + 4 * DE : 2 * QK_STEPS * (FP8 ? 2 : 1) + (V8 ? 4 : 8) * DE;
+  static constexpr int kStepMfma = 2 * QK_STEPS + (V8 ? 1 : 4) * DE;
+  static constexpr int kFirstReads = KS ? QK_STEPS : 2 * QK_STEPS * (FP8 ? 2 : 1);
   // S^T rows of key block 1 sit this many K rows after block 0's
   static constexpr int kBlock1Rows = V8 ? 16 : 32;
   static __device__ __forceinline__ int kswz(int row) {
@@ -276,13 +295,15 @@ struct QTile {
 
   const Params& p;
   unsigned char* smem;
-  int lane, wave, l32, hl, N, bh, m0, wrow0, qrow, qsrc, t_lo, NK;
-  int klo_m1, khi;          // keys visible to the lane's row: klo_m1 < key <= khi
+  int lane, wave, l32, hl, N, bh, m0, wrow0, t_lo, NK;
+  int kh;                   // key split: the 32-key half of every tile this wave takes
+  int qrow[NJ], qsrc[NJ];   // the lane's row in each row block
+  int klo_m1[NJ], khi[NJ];  // keys visible to the lane's rows: klo_m1 < key <= khi
   int f_lo, f_hi;           // local tiles [f_lo, f_hi) are FULL for this wave
   size_t head;
-  QFrag qf[QK_STEPS];
+  QFrag qf[NJ * QK_STEPS];  // [row block][k-step]
   // Q as loaded: 16-byte pieces, two per k-step for fp8
-  static constexpr int QRAW = FP8 ? 2 * QK_STEPS : QK_STEPS;
+  static constexpr int QRAW = NJ * (FP8 ? 2 * QK_STEPS : QK_STEPS);
   i32x4 qraw[QRAW];
   float qscale;
   int kdma[KLD], vdma[VLD];
@@ -296,15 +317,16 @@ struct QTile {
   const int* pg_ids;
   int pg_h, pg_len, k_next, v_next;
 
-  float m_ref;              // reference (log2 units) of the exponentials; -inf: none yet
-  float m_use;              // m_ref, or 0 while it is -inf
-  float limit;              // largest tile sum of P that keeps m_ref (-1 while it is -inf)
+  // per row block of the lane:
+  float m_ref[NJ];          // reference (log2 units) of the exponentials; -inf: none yet
+  float m_use[NJ];          // m_ref, or 0 while it is -inf
+  float limit[NJ];          // largest tile sum of P that keeps m_ref (-1 while it is -inf)
+  float l_run[NJ];          // this lane's share of the row sum
   float c_next;             // fp8: score scale of the next tile, loaded a step ahead
-  float l_run;              // this lane's share of the row sum
   int vq0, vq1;             // fp8 V: scale exponents (E8M0) of tiles i and i+1 at step i+1
-  f32x16 oacc[DE];
-  f32x16 S[2][2];           // S^T of two tiles: [buffer][key block]
-  bf16x8 P[2][4];           // P of two tiles: [buffer][k-step]
+  f32x16 oacc[NJ * DE];     // [row block][32-dim block]
+  f32x16 S[2][2];           // S^T of two tiles: [buffer][key block] (key split: [buffer][row block])
+  bf16x8 P[2][4];           // P of two tiles: [buffer][k-step] (key split: [buffer][2 row block + k-step])
   i32x8 P8[2];              // fp8 V: P of two tiles as fp8 bytes, byte k = key 32 hl + k
 
   // offs: the document offsets (p.doc, or a copy of them in LDS that the
@@ -326,17 +348,21 @@ struct QTile {
     bh = bh_;
     m0 = qt * BM;
     const int m1 = min(m0 + BM, N);
-    wrow0 = m0 + wave * 32;
-    qrow = wrow0 + l32;
+    kh = KS ? wave >> 1 : 0;
+    wrow0 = m0 + (KS ? (wave & 1) * 64 : wave * 32);
     // a row past N (ragged last Q tile) computes row N - 1's result, which is
     // never stored: it stays finite and takes no extra slow-path steps
-    qsrc = min(qrow, N - 1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      qrow[j] = wrow0 + 32 * j + l32;
+      qsrc[j] = min(qrow[j], N - 1);
+    }
     head = (size_t)bh * N;
     if constexpr (!FP8 && !PG) {
       if (early) load_q();
     }
 
-    const int wr0 = min(wrow0, N - 1), wr1 = min(wrow0 + 31, N - 1);
+    const int wr0 = min(wrow0, N - 1), wr1 = min(wrow0 + 32 * NJ - 1, N - 1);
     RowSpans sp;
     if constexpr (PG) {
       // keys [0, hi(row)]: causal prefill rows sit at positions len - N + row
@@ -346,7 +372,8 @@ struct QTile {
       pg_len = min(max(p.pg_lens[s * p.len_stride_s + qt * p.len_stride_b], 0), p.pg_max * p.pg_page);
       const int pos0 = pg_len - N;
       auto span = [&](int r) -> KeySpan { return {0, p.pg_causal ? min(pg_len - 1, pos0 + r) : pg_len - 1}; };
-      sp.lane = span(qsrc);
+      sp.lane = span(qsrc[0]);
+      sp.lane2 = sp.lane;
       sp.wave_first = span(wr0);
       sp.wave_last = span(wr1);
       sp.tile_first = span(m0);
@@ -366,7 +393,7 @@ struct QTile {
       k_next = 0;
       v_next = 0;
     } else {
-      sp = row_spans(p.mask, p.window, offs, p.nd, N, m0, m1 - 1, wr0, wr1, qsrc);
+      sp = row_spans(p.mask, p.window, offs, p.nd, N, m0, m1 - 1, wr0, wr1, qsrc[0], qsrc[NJ - 1]);
       // the tile's and the wave's spans are uniform; offsets read through a
       // pointer that may be in LDS come back in VGPRs, so say so
       auto uniform = [](KeySpan k) {
@@ -420,8 +447,12 @@ struct QTile {
     }
 
     // ---- per-lane state of the loop
-    klo_m1 = sp.lane.lo - 1;
-    khi = sp.lane.hi;
+    klo_m1[0] = sp.lane.lo - 1;
+    khi[0] = sp.lane.hi;
+    if constexpr (KS) {
+      klo_m1[NJ - 1] = sp.lane2.lo - 1;
+      khi[NJ - 1] = sp.lane2.hi;
+    }
     // FULL range of this wave's 32 rows (a contiguous run of tiles), local indices
     full_tiles(sp.wave_first, sp.wave_last, BN, &f_lo, &f_hi);
     f_lo = min(max(f_lo - t_lo, 0), NK);
@@ -433,7 +464,7 @@ struct QTile {
     // kBlock1Rows further, same swizzle), chunk of half hl. With fp8 V the
     // rows are permuted so that lane (row l32, half hl) ends up holding keys
     // 32 hl .. 32 hl + 31 of the tile: row 8j + 4h + t reads key 32h + 4j + t.
-    const int krow = V8 ? 32 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3) : l32;
+    const int krow = V8 ? 32 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3) : 32 * kh + l32;
     constexpr int KCH_STEP = FP8 ? 4 : 2;  // 16-byte chunks per k-step
 #pragma unroll
     for (int t = 0; t < QK_STEPS; ++t) {
@@ -464,18 +495,22 @@ struct QTile {
       // transposed V read: 16-lane group g, row rr of 4, 8-byte column piece cc
       const int g = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
       const int sv = swz_v<VROW>(4 * hl + rr);   // same for rows +16q and +8
+      // (key split: the wave's half starts 32 rows in; rows 32 apart share the swizzle)
 #pragma unroll
       for (int e = 0; e < DE; ++e)
-        vread[e] = (4 * hl + rr) * VROW + 16 * ((4 * e + 2 * (g & 1) + (cc >> 1)) ^ sv) + 8 * (cc & 1);
+        vread[e] = (32 * kh + 4 * hl + rr) * VROW + 16 * ((4 * e + 2 * (g & 1) + (cc >> 1)) ^ sv) + 8 * (cc & 1);
     }
 
-    m_ref = -INFINITY;
-    m_use = 0.f;
-    limit = -1.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      m_ref[j] = -INFINITY;
+      m_use[j] = 0.f;
+      limit[j] = -1.f;
+      l_run[j] = 0.f;
+    }
     c_next = tile_scale(0);
     vq0 = 127;                // the tile before the first (no P V there)
     vq1 = v_exponent(0);
-    l_run = 0.f;
   }
 
   // Q fragments: lane (row l32, half hl) holds the k-slots of half hl. The
@@ -489,16 +524,19 @@ struct QTile {
   }
   __device__ __forceinline__ void load_q() {
     if constexpr (FP8) {
-      const unsigned char* qp = (const unsigned char*)p.q + (head + qsrc) * D + 32 * hl;
+      const unsigned char* qp = (const unsigned char*)p.q + (head + qsrc[0]) * D + 32 * hl;
 #pragma unroll
       for (int t = 0; t < QK_STEPS; ++t) {
         qraw[2 * t] = gload16(qp + 64 * t);
         qraw[2 * t + 1] = gload16(qp + 64 * t + 16);
       }
     } else {
-      const __bf16* qp = (const __bf16*)p.q + (head + qsrc) * D + 8 * hl;
 #pragma unroll
-      for (int t = 0; t < QK_STEPS; ++t) qraw[t] = gload16(qp + 16 * t);
+      for (int j = 0; j < NJ; ++j) {
+        const __bf16* qp = (const __bf16*)p.q + (head + qsrc[j]) * D + 8 * hl;
+#pragma unroll
+        for (int t = 0; t < QK_STEPS; ++t) qraw[j * QK_STEPS + t] = gload16(qp + 16 * t);
+      }
     }
   }
   // waits until at most N vector-memory operations of this wave are
@@ -522,7 +560,7 @@ struct QTile {
                    : "n"(N)
                    : "memory");
 #pragma unroll
-    for (int t = 0; t < QK_STEPS; ++t) {
+    for (int t = 0; t < NJ * QK_STEPS; ++t) {
       if constexpr (FP8) {
         const i32x4 a = qraw[2 * t], b = qraw[2 * t + 1];
         qf[t] = (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -627,6 +665,11 @@ struct QTile {
         const i32x8 a1 = {a1l[0], a1l[1], a1l[2], a1l[3], a1h[0], a1h[1], a1h[2], a1h[3]};
         s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qf[t], s0, 0, 0, 0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qf[t], s1, 0, 0, 0, 0, 0, 0);
+      } else if constexpr (KS) {
+        // one read of the wave's 32 keys serves both row blocks
+        const bf16x8 a = *(const bf16x8*)(ksl + kread[t]);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[QK_STEPS + t], s1, 0, 0, 0);
       } else {
         const bf16x8 a0 = *(const bf16x8*)(ksl + kread[t]);
         const bf16x8 a1 = *(const bf16x8*)(ksl + kread[t] + kBlock1Rows * KROW);
@@ -658,8 +701,10 @@ struct QTile {
       }
       return;
     }
+    // key split: the wave's 32 keys are k-steps 0 and 1 (rows 16 q from its
+    // half's start); each V^T operand serves both row blocks
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < (KS ? 2 : 4); ++q) {
 #pragma unroll
       for (int e = 0; e < DE; ++e) {
         const unsigned char* vp = vsl + vread[e] + 16 * q * VROW;
@@ -667,13 +712,15 @@ struct QTile {
         const s16x4 hi =
             __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vp + 8 * VROW));
         const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), P[B][q], oacc[e], 0, 0, 0);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, vv);
+        oacc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[B][q], oacc[e], 0, 0, 0);
+        if constexpr (KS) oacc[DE + e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[B][2 + q], oacc[DE + e], 0, 0, 0);
       }
     }
   }
 
   // reference the exponentials subtract: fp8 P is formed 2^kPShiftFp8 times larger
-  __device__ __forceinline__ float m_exp() const { return V8 ? m_use - (float)kPShiftFp8 : m_use; }
+  __device__ __forceinline__ float m_exp(int j) const { return V8 ? m_use[j] - (float)kPShiftFp8 : m_use[j]; }
 
   // fp8 V: E8M0 exponent (biased by 127) of local tile i's power-of-two V scale
   __device__ __forceinline__ int v_exponent(int i) const {
@@ -692,15 +739,20 @@ struct QTile {
   // S[B] of local tile i: -inf where the key is not visible to the lane's row
   template <int B>
   __device__ __forceinline__ void mask(int i) {
-    // key of S[B][b][r] is n0 + 32b + 8(r/4) + 4hl + r%4 (fp8 V: n0 + 32hl + 16b + r)
+    // key of S[B][b][r] is n0 + 32b + 8(r/4) + r%4 (fp8 V: n0 + 16b + r; key
+    // split: n0 + 8(r/4) + r%4 in both row blocks b, n0 past the wave's half)
     // visible offsets kc: lo < kc <= hi (the interval ends before N)
-    const int n0 = (t_lo + i) * BN + (V8 ? 32 : 4) * hl;
-    const int hi = khi - n0;
-    const int lo = klo_m1 - n0;
+    const int n0 = (t_lo + i) * BN + (V8 ? 32 : 4) * hl + 32 * kh;
+    int lo[NJ], hi[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      hi[j] = khi[j] - n0;
+      lo[j] = klo_m1[j] - n0;
+    }
     // a bound no lane's keys of this tile cross is not tested (the causal
     // diagonal needs only the upper one, a window's far edge only the lower)
-    constexpr int kMaxKc = V8 ? 31 : 59;
-    const bool need_lo = __any(lo >= 0), need_hi = __any(hi < kMaxKc);
+    constexpr int kMaxKc = KS ? 27 : V8 ? 31 : 59;
+    const bool need_lo = __any(max(lo[0], lo[NJ - 1]) >= 0), need_hi = __any(min(hi[0], hi[NJ - 1]) < kMaxKc);
     if (need_lo && need_hi)
       mask_with<B, true, true>(lo, hi);
     else if (need_hi)
@@ -709,29 +761,53 @@ struct QTile {
       mask_with<B, true, false>(lo, hi);
   }
   template <int B, bool LO, bool HI>
-  __device__ __forceinline__ void mask_with(int lo, int hi) {
+  __device__ __forceinline__ void mask_with(const int (&lo)[NJ], const int (&hi)[NJ]) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kc = V8 ? 16 * b + r : 32 * b + 8 * (r >> 2) + (r & 3);
-        const bool vis = (!HI || kc <= hi) && (!LO || kc > lo);
+        constexpr int j0 = 0;
+        const int j = KS ? b : j0;
+        const int kc = KS ? 8 * (r >> 2) + (r & 3) : V8 ? 16 * b + r : 32 * b + 8 * (r >> 2) + (r & 3);
+        const bool vis = (!HI || kc <= hi[j]) && (!LO || kc > lo[j]);
         S[B][b][r] = vis ? S[B][b][r] : -INFINITY;
       }
   }
 
   // P[B] = 2^(S[B] c - m_use) rounded to bf16 as the B operand (k-step q covers
-  // keys 16q..16q+15 of the tile); returns the lane's fp32 sum of the values.
-  // The sum is a tree of plain adds: v_dot2 on the packed bf16 values would
-  // not issue while an MFMA is executing, these do.
+  // keys 16q..16q+15 of the tile; key split: P[B][2j + q] covers keys 16q ..
+  // 16q+15 of the wave's half for row block j); psum gets the lane's fp32 sum
+  // of the values (per row block). The sum is a tree of plain adds: v_dot2 on
+  // the packed bf16 values would not issue while an MFMA is executing, these do.
   template <int B>
-  __device__ __forceinline__ float exponentials(float c, float m_use) {
+  __device__ __forceinline__ void exponentials(float c, float (&psum)[NJ]) {
+    if constexpr (KS) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float e[16];
+        const float mj = m_exp(j);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            e[8 * q + jj] = fast_exp2(__builtin_fmaf(S[B][j][8 * q + jj], c, -mj));
+            P[B][2 * j + q][jj] = (__bf16)e[8 * q + jj];
+          }
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+          for (int jj = 0; jj < w; ++jj) e[jj] += e[jj + w];
+        psum[j] = e[0];
+      }
+      return;
+    }
     float e[32];
+    const float m0v = m_exp(0);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        e[8 * q + j] = fast_exp2(__builtin_fmaf(S[B][q >> 1][8 * (q & 1) + j], c, -m_use));
+        e[8 * q + j] = fast_exp2(__builtin_fmaf(S[B][q >> 1][8 * (q & 1) + j], c, -m0v));
         if constexpr (!V8) P[B][q][j] = (__bf16)e[8 * q + j];
       }
     if constexpr (V8) {
@@ -746,7 +822,21 @@ struct QTile {
     for (int w = 16; w >= 1; w >>= 1)
 #pragma unroll
       for (int j = 0; j < w; ++j) e[j] += e[j + w];
-    return e[0];
+    psum[0] = e[0];
+  }
+
+  // the row max of S[B] over the lane pair (l, l^32) for row block j (unscaled)
+  template <int B>
+  __device__ __forceinline__ float tile_row_max(int j) const {
+    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if constexpr (KS) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) mq[r & 3] = max3(mq[r & 3], S[B][j][r], S[B][j][r + 8]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mq[r & 3] = max3(mq[r & 3], S[B][0][r], S[B][1][r]);
+    }
+    return half_swap_max(max3(mq[0], mq[1], fmaxf(mq[2], mq[3])));
   }
 
   // First tile of the Q tile: the reference is the exact row max of its
@@ -754,35 +844,39 @@ struct QTile {
   // tile takes the slow path). Nothing is rescaled: l and acc are still 0.
   template <int B>
   __device__ __forceinline__ void set_reference(float c) {
-    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mq[r & 3] = max3(mq[r & 3], S[B][0][r], S[B][1][r]);
-    m_ref = half_swap_max(max3(mq[0], mq[1], fmaxf(mq[2], mq[3]))) * c;
-    m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    limit = m_ref == -INFINITY ? -1.f : kLimit;
+    for (int j = 0; j < NJ; ++j) {
+      m_ref[j] = tile_row_max<B>(j) * c;
+      m_use[j] = m_ref[j] == -INFINITY ? 0.f : m_ref[j];
+      limit[j] = m_ref[j] == -INFINITY ? -1.f : kLimit;
+    }
   }
 
   // Slow path for tile i in S[B]/P[B]: the reference becomes the exact row max
   // (if it rises), P is recomputed against it, and l and acc (which holds P V
   // of the tiles before i) are rescaled.
   template <int B>
-  __device__ __forceinline__ void rebase(float c, float& psum) {
-    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  __device__ __forceinline__ void rebase(float c, float (&psum)[NJ]) {
+    float alpha[NJ];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mq[r & 3] = max3(mq[r & 3], S[B][0][r], S[B][1][r]);
-    const float mt = half_swap_max(max3(mq[0], mq[1], fmaxf(mq[2], mq[3]))) * c;
-    const float m_new = fmaxf(m_ref, mt);
-    // 0 on a first move from -inf; 1 when nothing moves
-    const float alpha = m_new == m_ref ? 1.f : fast_exp2(m_ref - m_new);
-    m_ref = m_new;
-    m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    limit = m_ref == -INFINITY ? -1.f : kLimit;
-    psum = exponentials<B>(c, m_exp());
-    l_run *= alpha;
+    for (int j = 0; j < NJ; ++j) {
+      const float mt = tile_row_max<B>(j) * c;
+      const float m_new = fmaxf(m_ref[j], mt);
+      // 0 on a first move from -inf; 1 when nothing moves
+      alpha[j] = m_new == m_ref[j] ? 1.f : fast_exp2(m_ref[j] - m_new);
+      m_ref[j] = m_new;
+      m_use[j] = m_ref[j] == -INFINITY ? 0.f : m_ref[j];
+      limit[j] = m_ref[j] == -INFINITY ? -1.f : kLimit;
+    }
+    exponentials<B>(c, psum);
 #pragma unroll
-    for (int e = 0; e < DE; ++e)
+    for (int j = 0; j < NJ; ++j) {
+      l_run[j] *= alpha[j];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha;
+      for (int e = 0; e < DE; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[j * DE + e][r] *= alpha[j];
+    }
   }
 
   // One pipeline step at local tile i (PH = i mod U): S of tile i+1 and P V of
@@ -791,8 +885,112 @@ struct QTile {
   // reference before the exponentials, which are then formed once.
   // MASK: the step tests whether tile i is outside this wave's FULL range and
   // masks it then; the loop's bulk runs without (see loop()).
+  // ---- key split: one S buffer per row block, the step in three phases
+  // K operands of the wave's 32 keys of the tile in slot SLOT (both row blocks use them)
+  template <int SLOT>
+  __device__ __forceinline__ void ks_kread(bf16x8 (&kop)[QK_STEPS]) const {
+    const unsigned char* ksl = smem + SLOT * C::K_SLOT;
+#pragma unroll
+    for (int t = 0; t < QK_STEPS; ++t) kop[t] = *(const bf16x8*)(ksl + kread[t]);
+  }
+  template <int J>
+  __device__ __forceinline__ void ks_qk(const bf16x8 (&kop)[QK_STEPS]) {
+    f32x16 s0 = {};
+#pragma unroll
+    for (int t = 0; t < QK_STEPS; ++t)
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[t], qf[J * QK_STEPS + t], s0, 0, 0, 0);
+    S[0][J] = s0;
+  }
+  // P[B][2J + q] = 2^(S[0][J] c - m_use[J]) as bf16; returns the lane's sum
+  template <int B, int J>
+  __device__ __forceinline__ float ks_exps(float c) {
+    float e[16];
+    const float mj = m_use[J];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        e[8 * q + jj] = fast_exp2(__builtin_fmaf(S[0][J][8 * q + jj], c, -mj));
+        P[B][2 * J + q][jj] = (__bf16)e[8 * q + jj];
+      }
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int jj = 0; jj < w; ++jj) e[jj] += e[jj + w];
+    return e[0];
+  }
+  template <int J>
+  __device__ __forceinline__ void ks_set_reference(float c) {
+    m_ref[J] = tile_row_max<0>(J) * c;
+    m_use[J] = m_ref[J] == -INFINITY ? 0.f : m_ref[J];
+    limit[J] = m_ref[J] == -INFINITY ? -1.f : kLimit;
+  }
+  template <int B, int J>
+  __device__ __forceinline__ void ks_rebase(float c, float& psum) {
+    const float mt = tile_row_max<0>(J) * c;
+    const float m_new = fmaxf(m_ref[J], mt);
+    const float alpha = m_new == m_ref[J] ? 1.f : fast_exp2(m_ref[J] - m_new);
+    m_ref[J] = m_new;
+    m_use[J] = m_ref[J] == -INFINITY ? 0.f : m_ref[J];
+    limit[J] = m_ref[J] == -INFINITY ? -1.f : kLimit;
+    psum = ks_exps<B, J>(c);
+    l_run[J] *= alpha;
+#pragma unroll
+    for (int e = 0; e < DE; ++e)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[J * DE + e][r] *= alpha;
+  }
+  // Step at local tile i, S_i in S[0]: (1) P V of tile i-1 beside the
+  // exponentials of row block 0, (2) S of tile i+1 for block 0 beside the
+  // exponentials of block 1, (3) S of tile i+1 for block 1. A block's scores
+  // are overwritten only after its reference test (and rare rebase) used them.
+  template <int PH, bool FIRST, bool MASK>
+  __device__ __forceinline__ void ks_step(int i) {
+    constexpr int B = PH & 1;          // P[B] receives P_i
+    constexpr int BO = B ^ 1;          // P[BO] holds P_{i-1}
+    sync_tiles<(NS - 2) * L>();
+    const float c = p.scale_log2;
+    if constexpr (kEarlyRefill) refill<PH>();
+    if constexpr (MASK) {
+      if ((unsigned)(i - f_lo) >= (unsigned)(f_hi - f_lo)) mask<0>(i);
+    }
+    bf16x8 kop[QK_STEPS];
+    ks_kread<(PH + 1) % NS>(kop);
+    if constexpr (!FIRST) pv<(PH + NS - 1) % NS, BO>(127);
+    if constexpr (FIRST) ks_set_reference<0>(c);
+    float ps0 = ks_exps<B, 0>(c);
+    __builtin_amdgcn_sched_group_barrier(0x100, FIRST ? QK_STEPS : kStepReads, 0);
+    if constexpr (!FIRST) {
+#pragma unroll
+      for (int k = 0; k < 4 * DE; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      if (__builtin_expect(__any(!(ps0 <= limit[0])), 0)) ks_rebase<B, 0>(c, ps0);
+    }
+    l_run[0] += ps0;
+    ks_qk<0>(kop);
+    if constexpr (FIRST) ks_set_reference<1>(c);
+    float ps1 = ks_exps<B, 1>(c);
+#pragma unroll
+    for (int k = 0; k < QK_STEPS; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    }
+    if constexpr (!FIRST) {
+      if (__builtin_expect(__any(!(ps1 <= limit[1])), 0)) ks_rebase<B, 1>(c, ps1);
+    }
+    l_run[1] += ps1;
+    ks_qk<1>(kop);
+    if constexpr (!kEarlyRefill) refill<PH>();
+  }
+
   template <int PH, bool FIRST = false, bool MASK = true>
   __device__ __forceinline__ void step(int i) {
+    if constexpr (KS) {
+      ks_step<PH, FIRST, MASK>(i);
+      return;
+    }
     constexpr int B = PH & 1;          // S[B] holds S_i, P[B] receives P_i
     constexpr int BO = B ^ 1;          // S[BO] receives S_{i+1}, P[BO] holds P_{i-1}
     // {K_{i+1}, V_{i-1}} landed; every wave is done with K_i and V_{i-2}
@@ -825,10 +1023,11 @@ struct QTile {
     qk<(PH + 1) % NS, BO>();
     if constexpr (!FIRST) pv<(PH + NS - 1) % NS, BO>(vpv);
     if constexpr (FIRST) set_reference<B>(c);
-    float psum = exponentials<B>(c, m_exp());
+    float psum[NJ];
+    exponentials<B>(c, psum);
     // issue order: every LDS operand read of the step first, then each MFMA
     // followed by a run of the softmax VALU work
-    constexpr int kReads = FIRST ? 2 * QK_STEPS * (FP8 ? 2 : 1) : kStepReads;
+    constexpr int kReads = FIRST ? kFirstReads : kStepReads;
     constexpr int kMfma = FIRST ? 2 * QK_STEPS : kStepMfma;
     __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
@@ -848,10 +1047,13 @@ struct QTile {
     // a lane without a reference yet, or a tile sum past the limit, moves it
     // (before P V of the tile, which the next step issues)
     if constexpr (!FIRST) {
-      if (__builtin_expect(__any(!(psum <= limit)), 0)) rebase<B>(c, psum);
+      bool over = !(psum[0] <= limit[0]);
+      if constexpr (KS) over = over || !(psum[1] <= limit[1]);
+      if (__builtin_expect(__any(over), 0)) rebase<B>(c, psum);
     }
     // the sum of P itself (fp8 P: the sum of the scaled values times 2^-3)
-    l_run += V8 ? psum * (1.f / (1 << kPShiftFp8)) : psum;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) l_run[j] += V8 ? psum[j] * (1.f / (1 << kPShiftFp8)) : psum[j];
     if constexpr (!kEarlyRefill) refill<PH>();
   }
 
@@ -923,7 +1125,7 @@ struct QTile {
   // every DMA landed and every wave past its last LDS read.
   __device__ __forceinline__ void loop() {
 #pragma unroll
-    for (int e = 0; e < DE; ++e) oacc[e] = (f32x16){};
+    for (int e = 0; e < NJ * DE; ++e) oacc[e] = (f32x16){};
     // Q (issued first) and K_0 have landed once no more than the NS - 1
     // later prologue batches are outstanding (the counter drains in order);
     // those batches keep streaming under the first steps
@@ -952,26 +1154,90 @@ struct QTile {
 
   // O = acc / l, written once (and the LSE)
   __device__ __forceinline__ void epilogue() {
-    const float l_tot = half_swap_sum(l_run);
-    if (qrow < N) {
+    if constexpr (KS) {
+      // the two waves of a row pair each finish one row block: a wave hands
+      // over the other block's (acc, m, l) through LDS (the ring is free: the
+      // loop ended with every wave past its last read) and merges its own
+      // block with its partner's
+      const float l0 = half_swap_sum(l_run[0]), l1 = half_swap_sum(l_run[1]);
+      if (kh)
+        handover<0>(l0);
+      else
+        handover<1>(l1);
+      __syncthreads();
+      if (kh)
+        finish<1>(l1);
+      else
+        finish<0>(l0);
+      return;
+    }
+    const float l_tot = half_swap_sum(l_run[0]);
+    if (qrow[0] < N) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
       for (int e = 0; e < DE; ++e)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = 32 * e + 8 * g4 + 4 * hl;
           const float x0 = oacc[e][4 * g4 + 0] * inv, x1 = oacc[e][4 * g4 + 1] * inv;
           const float x2 = oacc[e][4 * g4 + 2] * inv, x3 = oacc[e][4 * g4 + 3] * inv;
-          if constexpr (OUT_F32) {
-            *(float4*)((float*)p.o + (head + qrow) * D + d0) = make_float4(x0, x1, x2, x3);
-          } else {
-            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-            const bf16x4 ov = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
-            *(bf16x4*)((__bf16*)p.o + (head + qrow) * D + d0) = ov;
-          }
+          store_o(qrow[0], 32 * e + 8 * g4 + 4 * hl, x0, x1, x2, x3);
         }
       if (p.lse != nullptr && hl == 0)
-        p.lse[head + qrow] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+        p.lse[head + qrow[0]] = l_tot > 0.f ? (m_ref[0] + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+
+  __device__ __forceinline__ void store_o(int row, int d0, float x0, float x1, float x2, float x3) const {
+    if constexpr (OUT_F32) {
+      *(float4*)((float*)p.o + (head + row) * D + d0) = make_float4(x0, x1, x2, x3);
+    } else {
+      typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+      const bf16x4 ov = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+      *(bf16x4*)((__bf16*)p.o + (head + row) * D + d0) = ov;
+    }
+  }
+
+  // key split: LDS region of row pair (wave & 1), row block J: the state of
+  // block J from the wave that does not finish it. Accumulators lane-major in
+  // 16-byte pieces (piece k of every lane, then piece k + 1), then (m, l) per lane.
+  __device__ __forceinline__ unsigned char* xchg(int J) const { return smem + ((wave & 1) * 2 + J) * kXchgBytes; }
+  template <int J>
+  __device__ __forceinline__ void handover(float l_tot) {
+    unsigned char* x = xchg(J);
+#pragma unroll
+    for (int e = 0; e < DE; ++e)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = oacc[J * DE + e];
+        *(f32x4*)(x + ((e * 4 + g) * 64 + lane) * 16) = (f32x4){a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+      }
+    *(float2*)(x + DE * 16 * 64 * 4 + lane * 8) = make_float2(m_ref[J], l_tot);
+  }
+  template <int J>
+  __device__ __forceinline__ void finish(float l_own) {
+    const unsigned char* x = xchg(J);
+    const float2 ml = *(const float2*)(x + DE * 16 * 64 * 4 + lane * 8);
+    // the merge of two partial states over disjoint keys (the combine of
+    // split-key attention): both to the larger reference
+    const float m1 = m_ref[J], m2 = ml.x;
+    const float m = fmaxf(m1, m2);
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - m);
+    const float a2 = m2 == -INFINITY ? 0.f : fast_exp2(m2 - m);
+    const float l_tot = l_own * a1 + ml.y * a2;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float w1 = a1 * inv, w2 = a2 * inv;
+    const int row = qrow[J];
+    if (row < N) {
+#pragma unroll
+      for (int e = 0; e < DE; ++e)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 o2 = *(const f32x4*)(x + ((e * 4 + g4) * 64 + lane) * 16);
+          const f32x16& a = oacc[J * DE + e];
+          store_o(row, 32 * e + 8 * g4 + 4 * hl, a[4 * g4] * w1 + o2[0] * w2, a[4 * g4 + 1] * w1 + o2[1] * w2,
+                  a[4 * g4 + 2] * w1 + o2[2] * w2, a[4 * g4 + 3] * w1 + o2[3] * w2);
+        }
+      if (p.lse != nullptr && hl == 0) p.lse[head + row] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
 };
@@ -1060,7 +1326,7 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
   }
 }
 
-template <int D, bool FP8, bool OUT_F32, int PG, bool V8>
+template <int D, bool FP8, bool OUT_F32, int PG, bool V8, bool KSPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8, V8>::LDS + (PG ? 4 * kPrefillMaxPages : 0)];
   int bh, w;
@@ -1092,7 +1358,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // round trips per workgroup); a barrier then frees the LDS for the ring
     const bool lds_offs = p.order == ORDER_DOC;
     const bool early = !FP8 && !PG && !lds_offs;
-    QTile<D, FP8, OUT_F32, PG, V8> a(p, smem, bh, tb, lds_offs ? (const int32_t*)(smem + 2 * NT * sizeof(int)) : p.doc,
+    QTile<D, FP8, OUT_F32, PG, V8, KSPLIT> a(p, smem, bh, tb, lds_offs ? (const int32_t*)(smem + 2 * NT * sizeof(int)) : p.doc,
                                      early);
     if (!early) {
       a.load_q();
@@ -1104,7 +1370,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
   if (p.pair && ta != tb) {
     // the first tile's loop ended with every wave past its last LDS read
-    QTile<D, FP8, OUT_F32, PG, V8> b(p, smem, bh, ta, p.doc, !FP8 && !PG);
+    QTile<D, FP8, OUT_F32, PG, V8, KSPLIT> b(p, smem, bh, ta, p.doc, !FP8 && !PG);
     if (FP8 || PG) {
       b.load_q();
       b.start_stream();
@@ -1128,12 +1394,12 @@ Params base_params(const void* q, const void* k, const void* v, void* o, float* 
   return p;
 }
 
-template <int D, bool FP8, bool OUT_F32, int PG, bool V8 = false>
+template <int D, bool FP8, bool OUT_F32, int PG, bool V8 = false, bool KSPLIT = false>
 hipError_t launch_p(Params& p, int BH, hipStream_t stream) {
   p.units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   p.units = BH * p.units_per_bh;
   const int grid = round_up8(p.units);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32, PG, V8>), dim3(grid), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32, PG, V8, KSPLIT>), dim3(grid), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1161,6 +1427,12 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     // end: they share the CU unevenly)
     p.order = ORDER_TILES;
     p.per_group = a.BH;
+  }
+  // the key-split layout for bf16 d = 64 from kKeySplitMinN keys: fewer LDS
+  // reads per step, at a per-Q-tile cost (the epilogue's merge) that short
+  // loops do not recover
+  if constexpr (D == 64 && !FP8) {
+    if (a.N >= kKeySplitMinN) return launch_p<D, FP8, OUT_F32, false, false, true>(p, a.BH, stream);
   }
   return launch_p<D, FP8, OUT_F32, false, V8>(p, a.BH, stream);
 }
