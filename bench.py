@@ -488,7 +488,27 @@ def seq_len_sweep(torch, A):
                              "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
                 log(f"sweep: d={d} {mask} N={N}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
                 del q, k, v, o
-    return {"sweep": "bf16 prefill TFLOP/s over sequence length", "rows": rows}
+    # few-tile causal grids: attn_fwd against attn_fwd_split (the costliest
+    # tiles' key ranges split in two, merged by a second kernel)
+    split_rows = []
+    for (B, H, N, d) in ((1, 4, 8192, 64), (1, 8, 4096, 64), (1, 16, 4096, 64), (1, 16, 2048, 128),
+                         (1, 16, 4096, 128), (1, 8, 8192, 128)):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(N + d + H)
+        q, k, v = (torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        nb = A.attn_fwd_split_workspace_size(B, H, N, d, "bf16", "causal")
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+        ms_f, _, _ = event_time_ms(lambda: A.attn_fwd(q, k, v, o, 1.0 / math.sqrt(d), "causal"), 20)
+        ms_s, _, _ = event_time_ms(lambda: A.attn_fwd_split(q, k, v, o, 1.0 / math.sqrt(d), "causal", workspace=ws), 20)
+        fl = 4.0 * d * B * H * N * (N + 1) / 2
+        split_rows.append({"B": B, "H": H, "N": N, "d": d, "workspace_bytes": nb, "fwd_ms": round(ms_f, 5),
+                           "split_ms": round(ms_s, 5), "fwd_frac": round(fl / ms_f / 1e9 / PEAK_BF16_TFLOPS, 4),
+                           "split_frac": round(fl / ms_s / 1e9 / PEAK_BF16_TFLOPS, 4),
+                           "speedup": round(ms_f / ms_s, 3)})
+        log(f"sweep: split B={B} H={H} N={N} d={d}: {ms_f * 1e3:.1f} -> {ms_s * 1e3:.1f} us")
+        del q, k, v, o, ws
+    return {"sweep": "bf16 prefill TFLOP/s over sequence length", "rows": rows, "split_rows": split_rows}
 
 
 def main():

@@ -116,6 +116,42 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
                      float* lse, void* stream);
 
 /*
+ * attn_fwd_split_workspace_size -- bytes of workspace attn_fwd_split needs
+ * for this shape and mask: 0 when the launch is not split (fp32 inputs, masks
+ * other than CAUSAL and PREFIX_LM, or more than about 1.5 query tiles of 128
+ * rows per workgroup slot of the GPU), else B*H * (split tiles) * 2 * 128 *
+ * (d + 1) * 4 bytes. Host-only; 0 for arguments attn_fwd would reject.
+ */
+size_t attn_fwd_split_workspace_size(int B, int H, int N, int d, attn_dtype in_dtype,
+                                     attn_mask mask, int window);
+
+/*
+ * attn_fwd_split -- attn_fwd, with the key range of the costliest query tiles
+ * split in two for grids with few query tiles per workgroup slot (there the
+ * costliest tile alone sets the launch time). Each part runs the same online
+ * softmax over its keys and writes its normalised output and LSE to the
+ * workspace; a second kernel merges the two parts of each split tile as
+ * O = sum_i exp(L_i - L) O_i with L = log sum_i exp(L_i) (the split-KV merge
+ * of "Flash MSA ...", "Understanding Flash MSA Core Mechanics", applied to the
+ * key dimension of prefill), and writes O and the LSE.
+ *   Arguments as attn_fwd, plus:
+ *   workspace, workspace_bytes : device memory of at least
+ *             attn_fwd_split_workspace_size(...) bytes, 16-byte aligned, owned
+ *             by the caller; contents need not be initialised. When that size
+ *             is 0 the call is attn_fwd and the workspace is not touched (it
+ *             may be NULL). Too small or NULL otherwise -> ATTN_ERR_WORKSPACE.
+ * Two kernels are enqueued on the stream; calls that share a workspace must
+ * not overlap.
+ */
+attn_status attn_fwd_split(const void* q, const void* k, const void* v, void* o,
+                           int B, int H, int N, int d,
+                           attn_dtype in_dtype, attn_dtype out_dtype,
+                           float scale, attn_mask mask, int window,
+                           const int32_t* doc_offsets, int num_docs,
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * attn_fwd_fp8 -- prefill with block-quantised fp8 Q and K and bf16 V
  * ("FlashAttention-3: Warp Specialization ...", "FP8 Block Quantization").
  *   q8, k8   : [B, H, N, d] OCP E4M3FN bytes.

@@ -437,3 +437,33 @@ def test_noalloc_decode_rejects_work_beyond_its_array():
                                          None) == _lib.ATTN_ERR_UNSUPPORTED
     # the benchmark's decode fits
     assert lib.attn_decode_paged_workspace_size(64, 32, 128, 512, 16) <= (16 << 20)
+
+
+def test_split_workspace_size_and_rejects():
+    """attn_fwd_split_workspace_size: B*H * split tiles * 2 * 128 * (d + 1) * 4
+    bytes when the plan splits (causal N = 8192, 4 heads: the 32 costliest of 64
+    tiles), 0 otherwise; attn_fwd_split refuses a missing or short workspace
+    before anything runs (FAKE pointers: nothing is dereferenced)."""
+    lib = _lib.load()
+    causal, prefix, none = _lib.MASKS["causal"], _lib.MASKS["prefix_lm"], _lib.MASKS["none"]
+    bf16, f32 = _lib.ATTN_BF16, _lib.ATTN_F32
+    assert lib.attn_fwd_split_workspace_size(1, 4, 8192, 64, bf16, causal, 0) == 4 * 32 * 2 * 128 * 65 * 4
+    assert lib.attn_fwd_split_workspace_size(1, 16, 4096, 128, bf16, causal, 0) == 16 * 16 * 2 * 128 * 129 * 4
+    # 2500 rows in 20 tiles of 2, 4, .., 40 key tiles (the last ragged): the 10 costliest split
+    assert lib.attn_fwd_split_workspace_size(1, 4, 2500, 64, bf16, causal, 0) == 4 * 10 * 2 * 128 * 65 * 4
+    assert lib.attn_fwd_split_workspace_size(1, 8, 2048, 128, bf16, prefix, 512) > 0
+    for args in [(4, 16, 2048, 64, bf16, causal, 0),      # two tiles per slot: not split
+                 (1, 16, 4096, 64, bf16, causal, 0),      # one tile per slot, loops too short to pay
+                 (1, 2, 300, 64, bf16, causal, 0),        # tiles too cheap
+                 (1, 4, 8192, 64, f32, causal, 0),        # fp32 path
+                 (1, 4, 8192, 64, bf16, none, 0),         # equal-cost tiles
+                 (1, 1, 64, 64, bf16, causal, 0),         # one tile of one key tile
+                 (1, 1, 4096, 96, bf16, causal, 0)]:      # unsupported d
+        assert lib.attn_fwd_split_workspace_size(*args) == 0, args
+    need = lib.attn_fwd_split_workspace_size(1, 4, 8192, 64, bf16, causal, 0)
+    base = (FAKE, FAKE, FAKE, FAKE, 1, 4, 8192, 64, bf16, bf16, 0.125, causal, 0, None, 0, None)
+    assert lib.attn_fwd_split(*base, None, 0, None) == _lib.ATTN_ERR_WORKSPACE
+    assert lib.attn_fwd_split(*base, FAKE, need - 1, None) == _lib.ATTN_ERR_WORKSPACE
+    assert lib.attn_fwd_split(*base, FAKE_MIS, need, None) == _lib.ATTN_ERR_INVALID_ARG
+    bad = (FAKE, FAKE, FAKE, FAKE, 1, 4, 8192, 64, bf16, bf16, 0.0, causal, 0, None, 0, None)
+    assert lib.attn_fwd_split(*bad, FAKE, need, None) == _lib.ATTN_ERR_INVALID_ARG

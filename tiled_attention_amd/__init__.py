@@ -7,6 +7,8 @@ same entry-point names, the build script and the seeded workload generators.
 
 from ._lib import (  # noqa: F401
     attn_fwd,
+    attn_fwd_split,
+    attn_fwd_split_workspace_size,
     attn_fwd_fp8,
     attn_fwd_fp8_full,
     attn_quant_fp8_block,

@@ -24,6 +24,9 @@ _c_int, _c_float, _p, _size = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, cty
 _PROTOS = {
     "attn_fwd": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                           _c_int, _c_int, _p, _c_int, _p, _p]),
+    "attn_fwd_split_workspace_size": (_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "attn_fwd_split": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                _c_int, _c_int, _p, _c_int, _p, _p, _size, _p]),
     "attn_fwd_fp8": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                               _c_int, _c_int, _p, _c_int, _p, _p]),
     "attn_fwd_fp8_full": (_c_int, [_p, _p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -164,6 +167,38 @@ def attn_fwd(q, k, v, o, scale, mask="none", window=0, doc_offsets=None, lse=Non
     _dev(q, k, v, o, lse)
     _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, _dtype_code(q), _dtype_code(o),
                            float(scale), MASKS[mask], int(window), dp, nd, _ptr(lse), _stream(stream)))
+    return o
+
+
+def attn_fwd_split_workspace_size(B, H, N, d, dtype="bf16", mask="causal", window=0):
+    """Bytes of workspace attn_fwd_split needs (0: the launch is not split)."""
+    _require(mask in MASKS, f"unknown mask {mask!r}")
+    _require(dtype in ("bf16", "f32"), "dtype is 'bf16' or 'f32'")
+    return int(load().attn_fwd_split_workspace_size(int(B), int(H), int(N), int(d),
+                                                     ATTN_BF16 if dtype == "bf16" else ATTN_F32,
+                                                     MASKS[mask], int(window)))
+
+
+def attn_fwd_split(q, k, v, o, scale, mask="causal", window=0, doc_offsets=None, lse=None, workspace=None,
+                   stream=None):
+    """attn_fwd with the costliest query tiles' key ranges split in two; workspace:
+    a device uint8 tensor of attn_fwd_split_workspace_size(...) bytes (None
+    when that size is 0)."""
+    f32, bf16, u8, _ = _dtypes()
+    _require(q.dim() == 4, "q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    _spec(q, "q", q.shape, (f32, bf16))
+    _spec(k, "k", q.shape, (q.dtype,))
+    _spec(v, "v", q.shape, (q.dtype,))
+    _spec(o, "o", q.shape, (f32, bf16))
+    _spec(lse, "lse", (B, H, N), (f32,), optional=True)
+    dp, nd = _docs(mask, doc_offsets)
+    if workspace is not None:
+        _require(workspace.dtype == u8 and workspace.dim() == 1, "workspace must be a 1-D uint8 tensor")
+    _dev(q, k, v, o, lse, workspace)
+    _check(load().attn_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d, _dtype_code(q), _dtype_code(o),
+                                 float(scale), MASKS[mask], int(window), dp, nd, _ptr(lse), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel(), _stream(stream)))
     return o
 
 

@@ -66,9 +66,12 @@ attn_status launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR
 
 extern "C" {
 
-attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
-                     attn_dtype in_dtype, attn_dtype out_dtype, float scale, attn_mask mask, int window,
-                     const int32_t* doc_offsets, int num_docs, float* lse, void* stream) {
+// Shared by attn_fwd and attn_fwd_split: validation, then the launch (with
+// the split-key plan when a workspace is given and the plan splits).
+static attn_status fwd_dense(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                             attn_dtype in_dtype, attn_dtype out_dtype, float scale, attn_mask mask, int window,
+                             const int32_t* doc_offsets, int num_docs, float* lse, void* workspace,
+                             size_t workspace_bytes, bool split, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_INVALID_ARG;
   if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID_ARG;
@@ -92,7 +95,44 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, int B
   a.in_f32 = in_dtype == ATTN_F32;
   a.out_f32 = out_dtype == ATTN_F32;
   a.fp8 = false;
+  if (split) {
+    const size_t need = attn::fwd_split_workspace_bytes(a);
+    if (need > 0) {
+      if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+      if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+      a.workspace = workspace;
+    }
+  }
   return launched(attn::launch_fwd(a, (hipStream_t)stream));
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                     attn_dtype in_dtype, attn_dtype out_dtype, float scale, attn_mask mask, int window,
+                     const int32_t* doc_offsets, int num_docs, float* lse, void* stream) {
+  return fwd_dense(q, k, v, o, B, H, N, d, in_dtype, out_dtype, scale, mask, window, doc_offsets, num_docs, lse,
+                   nullptr, 0, false, stream);
+}
+
+size_t attn_fwd_split_workspace_size(int B, int H, int N, int d, attn_dtype in_dtype, attn_mask mask, int window) {
+  if (check_dims(B, H, N, d) != ATTN_OK) return 0;
+  if (in_dtype != ATTN_F32 && in_dtype != ATTN_BF16) return 0;
+  if (mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_PREFIX_LM) return 0;
+  if (!valid_mask(mask, window, nullptr, 0)) return 0;
+  attn::FwdArgs a{};
+  a.BH = B * H;
+  a.N = N;
+  a.d = d;
+  set_mask(a, mask, window, nullptr, 0, N);
+  a.in_f32 = in_dtype == ATTN_F32;
+  return attn::fwd_split_workspace_bytes(a);
+}
+
+attn_status attn_fwd_split(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                           attn_dtype in_dtype, attn_dtype out_dtype, float scale, attn_mask mask, int window,
+                           const int32_t* doc_offsets, int num_docs, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return fwd_dense(q, k, v, o, B, H, N, d, in_dtype, out_dtype, scale, mask, window, doc_offsets, num_docs, lse,
+                   workspace, workspace_bytes, true, stream);
 }
 
 static attn_status fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,

@@ -157,6 +157,8 @@ __device__ __forceinline__ int swz_v8(int row) {
   return ROWB == 64 ? (row >> 2) & 1 : (row >> 1) & 3;
 }
 
+constexpr int kMaxSplitUnits = 256;   // units per head of a split launch (entries of unit_tab)
+
 struct Params {
   const void* q;
   const void* k;
@@ -180,14 +182,23 @@ struct Params {
   // groups of `per_group` equal-cost units
   int order, groups, per_group;
   float scale_log2;
+  // split key ranges (ORDER_SPLIT): group r of units is entry r of unit_tab
+  // (Q tile | split << 12 | part << 13); the two parts of a split tile
+  // t >= split_t0 write their normalised outputs (fp32 [BM, d]) and LSEs to
+  // part_o / part_lse, at rows ((bh n_split + t - split_t0) 2 + part) BM
+  float* part_o;
+  float* part_lse;
+  int split_t0, n_split, split_units;
+  uint16_t unit_tab[kMaxSplitUnits];
 };
 
 enum UnitOrder {
   ORDER_NONE = 0,    // unit u -> (bh, w) = (u / units_per_bh, u % units_per_bh), XCD-grouped
   ORDER_DOC = 1,     // groups = Q tiles, costed by the keys their documents span; per group: the heads
   ORDER_SEQ = 2,     // groups = sequences of a paged prefill, costed by length; per group: heads x units
-  ORDER_TILES = 3    // one Q tile per unit, tile-major from the last tile down (costs never fall with
+  ORDER_TILES = 3,   // one Q tile per unit, tile-major from the last tile down (costs never fall with
                      // the tile index for these masks), heads innermost so a head stays on one XCD
+  ORDER_SPLIT = 4    // as ORDER_TILES, with the costliest tiles split into two key ranges (unit_tab)
 };
 constexpr int kKeySplitMinN = 4096;   // bf16 d = 64: the key-split layout from this length
 constexpr int kOrderMaxDocs = 8192;  // document offsets staged in LDS for the costing (and the LDS
@@ -297,6 +308,7 @@ struct QTile {
   unsigned char* smem;
   int lane, wave, l32, hl, N, bh, m0, wrow0, t_lo, NK;
   int kh;                   // key split: the 32-key half of every tile this wave takes
+  int part;                 // -1, or the key range (0, 1) of a split Q tile this workgroup takes
   int qrow[NJ], qsrc[NJ];   // the lane's row in each row block
   int klo_m1[NJ], khi[NJ];  // keys visible to the lane's rows: klo_m1 < key <= khi
   int f_lo, f_hi;           // local tiles [f_lo, f_hi) are FULL for this wave
@@ -337,8 +349,9 @@ struct QTile {
   // tile and takes microseconds of issue time; its memory latency then
   // overlaps it.
   __device__ __forceinline__ QTile(const Params& p_, unsigned char* smem_, int bh_, int qt, const int32_t* offs,
-                                   bool early = false)
+                                   bool early = false, int part_ = -1)
       : p(p_), smem(smem_) {
+    part = part_;
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave logic scalar
@@ -405,6 +418,13 @@ struct QTile {
       sp.wave_last = uniform(sp.wave_last);
       touched_tiles(sp.tile_first, sp.tile_last, BN, &t_lo, &NK);
       NK -= t_lo;
+      if (part >= 0) {
+        // one of the two key ranges of a split Q tile: part 0 takes the first
+        // half (rounded up) of its tiles, part 1 the rest
+        const int h = (NK + 1) >> 1;
+        t_lo += part ? h : 0;
+        NK = part ? NK - h : h;
+      }
     }
     // opaque to the optimizer: bounds it can reason about (NK >= 1, t_lo = 0
     // for causal masks) let it restructure the tile loop of the fp8 kernels
@@ -1182,19 +1202,32 @@ struct QTile {
           const float x2 = oacc[e][4 * g4 + 2] * inv, x3 = oacc[e][4 * g4 + 3] * inv;
           store_o(qrow[0], 32 * e + 8 * g4 + 4 * hl, x0, x1, x2, x3);
         }
-      if (p.lse != nullptr && hl == 0)
-        p.lse[head + qrow[0]] = l_tot > 0.f ? (m_ref[0] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      if (hl == 0) store_lse(qrow[0], l_tot > 0.f ? (m_ref[0] + __log2f(l_tot)) * kLn2 : -INFINITY);
     }
   }
 
+  // first row of this part's slice of the split outputs
+  __device__ __forceinline__ size_t part_row0() const {
+    return ((size_t)(bh * p.n_split + (m0 / BM - p.split_t0)) * 2 + part) * BM;
+  }
+  // O (or, for a part of a split Q tile, its normalised fp32 output) of one row, dims d0 .. d0 + 3
   __device__ __forceinline__ void store_o(int row, int d0, float x0, float x1, float x2, float x3) const {
-    if constexpr (OUT_F32) {
+    if (part >= 0) {
+      *(float4*)(p.part_o + (part_row0() + (row - m0)) * D + d0) = make_float4(x0, x1, x2, x3);
+    } else if constexpr (OUT_F32) {
       *(float4*)((float*)p.o + (head + row) * D + d0) = make_float4(x0, x1, x2, x3);
     } else {
       typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
       const bf16x4 ov = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
       *(bf16x4*)((__bf16*)p.o + (head + row) * D + d0) = ov;
     }
+  }
+  // the row's LSE (natural log): to lse if asked for; a split part's always goes to part_lse
+  __device__ __forceinline__ void store_lse(int row, float v) const {
+    if (part >= 0)
+      p.part_lse[part_row0() + (row - m0)] = v;
+    else if (p.lse != nullptr)
+      p.lse[head + row] = v;
   }
 
   // key split: LDS region of row pair (wave & 1), row block J: the state of
@@ -1237,7 +1270,7 @@ struct QTile {
           store_o(row, 32 * e + 8 * g4 + 4 * hl, a[4 * g4] * w1 + o2[0] * w2, a[4 * g4 + 1] * w1 + o2[1] * w2,
                   a[4 * g4 + 2] * w1 + o2[2] * w2, a[4 * g4 + 3] * w1 + o2[3] * w2);
         }
-      if (p.lse != nullptr && hl == 0) p.lse[head + row] = l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
+      if (hl == 0) store_lse(row, l_tot > 0.f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY);
     }
   }
 };
@@ -1329,13 +1362,18 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
 template <int D, bool FP8, bool OUT_F32, int PG, bool V8, bool KSPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8, V8>::LDS + (PG ? 4 * kPrefillMaxPages : 0)];
-  int bh, w;
-  if (p.order == ORDER_TILES) {
+  int bh, w, part = -1;
+  if (p.order == ORDER_TILES || p.order == ORDER_SPLIT) {
     const int u = blockIdx.x;
     if (u >= p.units) return;
     const int r = u / p.per_group;       // per_group = B*H
     bh = u - r * p.per_group;
     w = r;                               // tile n_qtiles - 1 - r
+    if (p.order == ORDER_SPLIT) {
+      const int e = p.unit_tab[r];
+      w = p.n_qtiles - 1 - min(e & 0xfff, p.n_qtiles - 1);
+      part = (e >> 12) & 1 ? (e >> 13) & 1 : -1;
+    }
   } else if (p.order != ORDER_NONE) {
     // ranks follow workgroup ids (the dispatch order); each XCD takes every 8th
     const int u = blockIdx.x;
@@ -1359,7 +1397,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const bool lds_offs = p.order == ORDER_DOC;
     const bool early = !FP8 && !PG && !lds_offs;
     QTile<D, FP8, OUT_F32, PG, V8, KSPLIT> a(p, smem, bh, tb, lds_offs ? (const int32_t*)(smem + 2 * NT * sizeof(int)) : p.doc,
-                                     early);
+                                     early, part);
     if (!early) {
       a.load_q();
       if (lds_offs) __syncthreads();
@@ -1394,13 +1432,137 @@ Params base_params(const void* q, const void* k, const void* v, void* o, float* 
   return p;
 }
 
+// Merge of the two key ranges of each split Q tile (one workgroup per tile):
+// from the parts' normalised outputs O_i and LSEs L_i, O = sum_i w_i O_i with
+// w_i = exp(L_i - L) and L = log sum_i exp(L_i) -- the combine of split-key
+// attention, as in the decode's combine. A row no part sees keys of gets
+// O = 0 and L = -inf.
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(NT) void split_combine_kernel(Params p) {
+  const int bh = blockIdx.x / p.n_split;
+  const int m0 = (p.split_t0 + blockIdx.x % p.n_split) * BM;
+  const size_t r0 = (size_t)blockIdx.x * 2 * BM;     // part 0's rows; part 1's follow
+  const size_t head = (size_t)bh * p.N;
+  constexpr int C4 = D / 4;
+  for (int i = threadIdx.x; i < BM * C4; i += NT) {
+    const int r = i / C4, c = i - r * C4;
+    const int row = m0 + r;
+    if (row >= p.N) break;
+    const float l0 = p.part_lse[r0 + r], l1 = p.part_lse[r0 + BM + r];
+    const float L = fmaxf(l0, l1);
+    float w0 = 0.f, w1 = 0.f, lse = -INFINITY;
+    if (L != -INFINITY) {
+      w0 = fast_exp2((l0 - L) * kLog2e);
+      w1 = fast_exp2((l1 - L) * kLog2e);
+      const float sum = w0 + w1;
+      lse = L + __log2f(sum) * kLn2;
+      w0 /= sum;
+      w1 /= sum;
+    }
+    const float4 a = *(const float4*)(p.part_o + (r0 + r) * D + 4 * c);
+    const float4 b = *(const float4*)(p.part_o + (r0 + BM + r) * D + 4 * c);
+    const float x0 = w0 * a.x + w1 * b.x, x1 = w0 * a.y + w1 * b.y;
+    const float x2 = w0 * a.z + w1 * b.z, x3 = w0 * a.w + w1 * b.w;
+    if constexpr (OUT_F32) {
+      *(float4*)((float*)p.o + (head + row) * D + 4 * c) = make_float4(x0, x1, x2, x3);
+    } else {
+      typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+      const bf16x4 ov = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+      *(bf16x4*)((__bf16*)p.o + (head + row) * D + 4 * c) = ov;
+    }
+    if (c == 0 && p.lse != nullptr) p.lse[head + row] = lse;
+  }
+}
+
 template <int D, bool FP8, bool OUT_F32, int PG, bool V8 = false, bool KSPLIT = false>
 hipError_t launch_p(Params& p, int BH, hipStream_t stream) {
+  if (p.order == ORDER_SPLIT) {
+    p.units_per_bh = p.split_units;
+    p.units = BH * p.units_per_bh;
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32, PG, V8, KSPLIT>), dim3(round_up8(p.units)), dim3(NT), 0,
+                       stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((split_combine_kernel<D, OUT_F32>), dim3(BH * p.n_split), dim3(NT), 0, stream, p);
+    return hipGetLastError();
+  }
   p.units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   p.units = BH * p.units_per_bh;
   const int grid = round_up8(p.units);
   hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32, PG, V8, KSPLIT>), dim3(grid), dim3(NT), 0, stream, p);
   return hipGetLastError();
+}
+
+// Split key ranges for grids of few Q tiles per workgroup slot (causal and
+// prefix-LM, bf16): with at most about one tile per slot the costliest tile
+// sets the launch time. Tiles costing more than half the costliest are cut
+// into two key ranges, and all units are dispatched costliest first. The
+// merge costs a second launch and a pass over the parts, so the plan splits
+// only where that measured faster: up to half a tile per slot when the
+// costliest tile holds at least 32 steps' worth of work (64-key tiles at
+// d = 64; half as many at d = 128), and up to 1.5 tiles per slot from 128.
+// A workgroup left alone on a CU runs faster than a paired one, which evens
+// out much of the imbalance below that. The plan depends only on the shape
+// and mask, so the size query and the launch agree.
+struct SplitPlan {
+  int units, t0, n_split;
+  uint16_t tab[kMaxSplitUnits];
+};
+constexpr int kSplitSlots = 512;            // workgroup slots: 256 CUs x 2 workgroups
+bool plan_split(const FwdArgs& a, SplitPlan* sp) {
+  if (a.in_f32 || a.fp8 || a.v8) return false;
+  if (a.mask != MASK_CAUSAL && a.mask != MASK_PREFIX_LM) return false;
+  const int T = (a.N + BM - 1) / BM;
+  if ((long long)a.BH * T * 2 > 3LL * kSplitSlots || 2 * T > kMaxSplitUnits || T > 0xfff) return false;
+  int cost[kMaxSplitUnits / 2];
+  int cmax = 0;
+  for (int t = 0; t < T; ++t) {
+    const int m1 = (t * BM + BM < a.N ? t * BM + BM : a.N) - 1;
+    int lo, hi;
+    touched_tiles(band_span(a.mask, a.window, a.N, t * BM), band_span(a.mask, a.window, a.N, m1), BN, &lo, &hi);
+    cost[t] = hi - lo;
+    cmax = cost[t] > cmax ? cost[t] : cmax;
+  }
+  const long long tiles = (long long)a.BH * T;
+  const int work = cmax * (a.d / 64);       // the costliest tile, in d = 64 steps
+  if (!((2 * tiles <= kSplitSlots && work >= 32) || (2 * tiles <= 3LL * kSplitSlots && work >= 128))) return false;
+  const int lim = (cmax + 1) / 2;
+  // the split tiles must be the last ones (costs never fall with t for these masks)
+  int t0 = T;
+  while (t0 > 0 && cost[t0 - 1] > lim) --t0;
+  for (int t = 0; t < t0; ++t)
+    if (cost[t] > lim) return false;
+  if (t0 == T) return false;
+  // units (cost, entry), costliest first; ties: later tile, then part 0
+  struct U { int c, e; };
+  U u[kMaxSplitUnits];
+  int n = 0;
+  for (int t = 0; t < T; ++t) {
+    if (t < t0) {
+      u[n++] = {cost[t], t};
+    } else {
+      const int h = (cost[t] + 1) / 2;
+      u[n++] = {h, t | 1 << 12};
+      u[n++] = {cost[t] - h, t | 1 << 12 | 1 << 13};
+    }
+  }
+  for (int i = 1; i < n; ++i) {            // insertion sort, n <= 256
+    const U x = u[i];
+    int j = i;
+    auto before = [](const U& p, const U& q) {
+      return p.c != q.c ? p.c > q.c : (p.e & 0xfff) != (q.e & 0xfff) ? (p.e & 0xfff) > (q.e & 0xfff) : p.e < q.e;
+    };
+    while (j > 0 && before(x, u[j - 1])) {
+      u[j] = u[j - 1];
+      --j;
+    }
+    u[j] = x;
+  }
+  sp->units = n;
+  sp->t0 = t0;
+  sp->n_split = T - t0;
+  for (int i = 0; i < n; ++i) sp->tab[i] = (uint16_t)u[i].e;
+  return true;
 }
 
 template <int D, bool FP8, bool OUT_F32, bool V8 = false>
@@ -1427,6 +1589,16 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     // end: they share the CU unevenly)
     p.order = ORDER_TILES;
     p.per_group = a.BH;
+    SplitPlan sp;
+    if (a.workspace != nullptr && plan_split(a, &sp)) {
+      p.order = ORDER_SPLIT;
+      p.split_units = sp.units;
+      p.split_t0 = sp.t0;
+      p.n_split = sp.n_split;
+      for (int i = 0; i < sp.units; ++i) p.unit_tab[i] = sp.tab[i];
+      p.part_o = (float*)a.workspace;
+      p.part_lse = p.part_o + (size_t)a.BH * sp.n_split * 2 * BM * D;
+    }
   }
   // the key-split layout for bf16 d = 64 from kKeySplitMinN keys: fewer LDS
   // reads per step, at a per-Q-tile cost (the epilogue's merge) that short
@@ -1466,6 +1638,12 @@ hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+size_t fwd_split_workspace_bytes(const FwdArgs& a) {
+  SplitPlan sp;
+  if (!plan_split(a, &sp)) return 0;
+  return (size_t)a.BH * sp.n_split * 2 * BM * (a.d + 1) * sizeof(float);
+}
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t stream) {
   if (a.v8) {

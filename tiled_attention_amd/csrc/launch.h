@@ -21,6 +21,7 @@ struct FwdArgs {
   int BH, N, d, mask, window;  // window clamped (clamp_window)
   float scale;
   bool in_f32, out_f32, fp8, v8;
+  void* workspace;      // nullable: split key ranges (attn_fwd_split) when the plan asks for it
 };
 
 // Prefill / cross-attention over a paged pool of 64-token pages.
@@ -67,6 +68,8 @@ constexpr int kDecodeSplitPages = 64;
 size_t decode_workspace_bytes(int S, int H, int d, int max_pages, int page_size);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// Workspace of the split-key prefill for this launch (0: the plan does not split).
+size_t fwd_split_workspace_bytes(const FwdArgs& a);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // The split-KV decode with its partial states in the library's static device
 // array (kNoAllocScratchBytes per GPU); a.workspace is ignored.
