@@ -117,10 +117,13 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
 
 /*
  * attn_fwd_split_workspace_size -- bytes of workspace attn_fwd_split needs
- * for this shape and mask: 0 when the launch is not split (fp32 inputs, masks
- * other than CAUSAL and PREFIX_LM, or more than about 1.5 query tiles of 128
- * rows per workgroup slot of the GPU), else B*H * (split tiles) * 2 * 128 *
- * (d + 1) * 4 bytes. Host-only; 0 for arguments attn_fwd would reject.
+ * for this shape and mask: 0 when the launch is not split, else B*H * (split
+ * tiles) * 2 * 128 * (d + 1) * 4 bytes. It splits only bf16 CAUSAL and
+ * PREFIX_LM launches with at most half a query tile (128 rows) per workgroup
+ * slot of the GPU (512 slots) whose costliest tile holds at least 32 key tiles
+ * of 64 (16 at d = 128), or at most 1.5 tiles per slot with at least 128 (64);
+ * elsewhere the merge does not pay. The query tiles that cost more than half
+ * the costliest are split. Host-only; 0 for arguments attn_fwd would reject.
  */
 size_t attn_fwd_split_workspace_size(int B, int H, int N, int d, attn_dtype in_dtype,
                                      attn_mask mask, int window);
