@@ -25,6 +25,8 @@ CASES = [
     (2, 2, 2200, 64, "causal", 0),
     (1, 2, 2048, 128, "causal", 0),
     (1, 3, 1500, 128, "prefix_lm", 700),
+    (1, 1, 4096, 64, "prefix_lm", 5000),  # window past N: every tile costs the same, all split
+    (1, 1, 8192, 128, "causal", 0),       # one head
 ]
 
 
