@@ -5,10 +5,10 @@
 Failure Modes, names register spills as a silent cause of slow kernels. On
 gfx950 a VGPR spill goes to scratch memory: no kernel may have one, nor any
 scratch. A spilled SGPR goes to a lane of a VGPR (v_writelane /
-v_readlane, no memory traffic); the paged kernels over 16-token pages hold
-four page descriptors per DMA batch and spill a few, so SGPR spills are
-allowed up to a small ceiling, and none at all in the kernels of the
-stated workloads' hot loops listed below."""
+v_readlane, no memory traffic). Every kernel is free of them but the
+d = 64 paged prefill over 16-token pages, which holds four page
+descriptors per DMA batch and spills three values outside its step (set-up
+and loop transitions): the ceiling below pins that."""
 
 from concurrent.futures import ThreadPoolExecutor
 
@@ -17,10 +17,9 @@ import pytest
 from tiled_attention_amd import build
 
 KERNEL_SOURCES = [s for s in build.SOURCES if s.endswith(".hip")]
-SGPR_SPILL_CEILING = 16
-# forward kernels of the stated workloads (bf16 d = 64 / d = 128, fp32 output for the checks)
-NO_SGPR_SPILL = ["fwd_mfma_kernelILi64ELb0ELb0ELi0ELb0E", "fwd_mfma_kernelILi128ELb0ELb0ELi0ELb0E",
-                 "fwd_mfma_kernelILi64ELb0ELb1ELi0ELb0E", "fwd_mfma_kernelILi128ELb0ELb1ELi0ELb0E"]
+SGPR_SPILL_CEILING = 3
+# every kernel but the d = 64, 16-token paged prefill (mangled: D, FP8, OUT_F32, PG, V8, KSPLIT)
+SGPR_SPILL_ALLOWED = ["fwd_mfma_kernelILi64ELb0ELb0ELi16E", "fwd_mfma_kernelILi64ELb0ELb1ELi16E"]
 
 
 @pytest.fixture(scope="module")
@@ -48,11 +47,11 @@ def test_no_vgpr_spill_and_no_scratch(usage):
 def test_sgpr_spills_bounded(usage):
     bad = {n: u["SGPRs Spill"] for n, u in usage.items() if u["SGPRs Spill"] > SGPR_SPILL_CEILING}
     assert not bad, bad
-    for key in NO_SGPR_SPILL:
-        hits = [n for n in usage if key in n]
-        assert hits, key
-        for n in hits:
-            assert usage[n]["SGPRs Spill"] == 0, (n, usage[n])
+    for key in SGPR_SPILL_ALLOWED:
+        assert any(key in n for n in usage), key
+    spilled = {n: u["SGPRs Spill"] for n, u in usage.items()
+               if u["SGPRs Spill"] and not any(key in n for key in SGPR_SPILL_ALLOWED)}
+    assert not spilled, spilled
 
 
 def test_forward_kernels_keep_two_waves_per_simd(usage):

@@ -178,6 +178,7 @@ struct Params {
   const int32_t* pg_table;
   const int32_t* pg_lens;
   int H, pg_stride_s, pg_stride_b, len_stride_s, len_stride_b, pg_max, pg_pool, pg_causal, pg_page;
+  int pg_cap;          // pg_max * pg_page: the longest list in tokens
   // heaviest-first dispatch (order != ORDER_NONE): units come in `groups`
   // groups of `per_group` equal-cost units
   int order, groups, per_group;
@@ -349,7 +350,7 @@ struct QTile {
   // tile and takes microseconds of issue time; its memory latency then
   // overlaps it.
   __device__ __forceinline__ QTile(const Params& p_, unsigned char* smem_, int bh_, int qt, const int32_t* offs,
-                                   bool early = false, int part_ = -1)
+                                   bool early = false, int part_ = -1, int seq = 0)
       : p(p_), smem(smem_) {
     part = part_;
     const int tid = threadIdx.x;
@@ -379,10 +380,12 @@ struct QTile {
     RowSpans sp;
     if constexpr (PG) {
       // keys [0, hi(row)]: causal prefill rows sit at positions len - N + row
-      const int s = bh / p.H;
+      // seq = bh / H, from the caller: the quotient's intermediates would
+      // otherwise stay live across a paired tile's loop
+      const int s = seq;
       pg_h = bh - s * p.H;
       const int32_t* list = p.pg_table + (size_t)s * p.pg_stride_s + (size_t)qt * p.pg_stride_b;
-      pg_len = min(max(p.pg_lens[s * p.len_stride_s + qt * p.len_stride_b], 0), p.pg_max * p.pg_page);
+      pg_len = min(max(p.pg_lens[s * p.len_stride_s + qt * p.len_stride_b], 0), p.pg_cap);
       const int pos0 = pg_len - N;
       auto span = [&](int r) -> KeySpan { return {0, p.pg_causal ? min(pg_len - 1, pos0 + r) : pg_len - 1}; };
       sp.lane = span(qsrc[0]);
@@ -397,7 +400,7 @@ struct QTile {
       // pool): one per tile, or four with 16-token pages, at most the list's
       // pg_max <= kPrefillMaxPages entries
       int* ids = (int*)(smem + C::LDS);
-      const int n_ids = min(NK * (BN / p.pg_page), p.pg_max);
+      const int n_ids = min(NK * (BN / PG), p.pg_max);   // PG: the page size
       for (int i = tid; i < n_ids; i += NT) ids[i] = min(max(list[i], 0), p.pg_pool - 1);
       __syncthreads();
       pg_ids = ids;
@@ -1167,7 +1170,13 @@ struct QTile {
     for (; i + U <= bulk_end; i += U) run_steps_full(i, std::make_integer_sequence<int, U>{});
     for (; i + U <= NK; i += U) run_steps(i, std::make_integer_sequence<int, U>{});
     run_tail(i, std::make_integer_sequence<int, U - 1>{});
-    if (NK > 0) run_drain((NK - 1) % U, std::make_integer_sequence<int, U>{});
+    {
+      // the count re-read through an opaque copy: a test of it formed before
+      // the loop would otherwise be held (and spilled) across it
+      int nk = NK;
+      asm volatile("" : "+s"(nk));
+      if (nk > 0) run_drain((nk - 1) % U, std::make_integer_sequence<int, U>{});
+    }
     // drain the DMA tail before the LDS is reused
     sync_tiles<0>();
   }
@@ -1316,7 +1325,7 @@ __device__ void ordered_unit(const Params& p, unsigned char* smem, int u, int* b
       const KeySpan l = doc_span(causal, offs[d], offs[d + 1], p.N, m1 - 1);
       c = l.hi / BN - f.lo / BN + 1;
     } else {
-      c = min(max(p.pg_lens[tid], 0), p.pg_max * p.pg_page);
+      c = min(max(p.pg_lens[tid], 0), p.pg_cap);
     }
     // the ranking's key (attn_common.h): by cost, then by index
     cost[tid] = (int)rank_key(c, tid);
@@ -1390,6 +1399,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // the longer Q tile first; Q is loaded before the tile stream's first DMAs,
   // so the two latencies overlap
   const int ta = w, tb = p.n_qtiles - 1 - w;
+  const int seq = PG ? __builtin_amdgcn_readfirstlane(bh / p.H) : 0;   // paged: the sequence
   {
     // with the ordering's LDS copy of the document offsets, the spans are
     // searched there (a search in global memory costs several dependent
@@ -1397,7 +1407,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const bool lds_offs = p.order == ORDER_DOC;
     const bool early = !FP8 && !PG && !lds_offs;
     QTile<D, FP8, OUT_F32, PG, V8, KSPLIT> a(p, smem, bh, tb, lds_offs ? (const int32_t*)(smem + 2 * NT * sizeof(int)) : p.doc,
-                                     early, part);
+                                     early, part, seq);
     if (!early) {
       a.load_q();
       if (lds_offs) __syncthreads();
@@ -1408,7 +1418,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
   if (p.pair && ta != tb) {
     // the first tile's loop ended with every wave past its last LDS read
-    QTile<D, FP8, OUT_F32, PG, V8, KSPLIT> b(p, smem, bh, ta, p.doc, !FP8 && !PG);
+    // opaque copies: products of these the first tile's set-up formed are
+    // recomputed here rather than held (and spilled) across its loop
+    int bh_b = bh, seq_b = seq;
+    asm volatile("" : "+s"(bh_b), "+s"(seq_b));
+    QTile<D, FP8, OUT_F32, PG, V8, KSPLIT> b(p, smem, bh_b, ta, p.doc, !FP8 && !PG, -1, seq_b);
     if (FP8 || PG) {
       b.load_q();
       b.start_stream();
@@ -1623,6 +1637,7 @@ hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
   p.pg_pool = a.num_pages;
   p.pg_causal = a.causal ? 1 : 0;
   p.pg_page = a.page_size;
+  p.pg_cap = a.max_pages * a.page_size;
   p.pair = p.pg_causal;
   const int units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
   // cross-attention lists keep the natural order: ranking them (by length)
