@@ -798,32 +798,13 @@ struct QTile {
   }
 
   // P[B] = 2^(S[B] c - m_use) rounded to bf16 as the B operand (k-step q covers
-  // keys 16q..16q+15 of the tile; key split: P[B][2j + q] covers keys 16q ..
-  // 16q+15 of the wave's half for row block j); psum gets the lane's fp32 sum
-  // of the values (per row block). The sum is a tree of plain adds: v_dot2 on
-  // the packed bf16 values would not issue while an MFMA is executing, these do.
+  // keys 16q..16q+15 of the tile); psum gets the lane's fp32 sum of the
+  // values. The sum is a tree of plain adds: v_dot2 on the packed bf16 values
+  // would not issue while an MFMA is executing, these do. (The key-split
+  // layout forms its exponentials per row block: ks_exps.)
   template <int B>
   __device__ __forceinline__ void exponentials(float c, float (&psum)[NJ]) {
-    if constexpr (KS) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        float e[16];
-        const float mj = m_exp(j);
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            e[8 * q + jj] = fast_exp2(__builtin_fmaf(S[B][j][8 * q + jj], c, -mj));
-            P[B][2 * j + q][jj] = (__bf16)e[8 * q + jj];
-          }
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-          for (int jj = 0; jj < w; ++jj) e[jj] += e[jj + w];
-        psum[j] = e[0];
-      }
-      return;
-    }
+    static_assert(!KS, "the key-split step uses ks_exps");
     float e[32];
     const float m0v = m_exp(0);
 #pragma unroll
@@ -1010,10 +991,14 @@ struct QTile {
 
   template <int PH, bool FIRST = false, bool MASK = true>
   __device__ __forceinline__ void step(int i) {
-    if constexpr (KS) {
+    if constexpr (KS)
       ks_step<PH, FIRST, MASK>(i);
-      return;
-    }
+    else
+      step32<PH, FIRST, MASK>(i);
+  }
+  // the 32-row layout's step
+  template <int PH, bool FIRST, bool MASK>
+  __device__ __forceinline__ void step32(int i) {
     constexpr int B = PH & 1;          // S[B] holds S_i, P[B] receives P_i
     constexpr int BO = B ^ 1;          // S[BO] receives S_{i+1}, P[BO] holds P_{i-1}
     // {K_{i+1}, V_{i-1}} landed; every wave is done with K_i and V_{i-2}
