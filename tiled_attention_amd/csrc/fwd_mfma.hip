@@ -169,7 +169,7 @@ struct Params {
   const float* k_scale;
   const float* v_scale;
   const int32_t* doc;
-  int N, mask, window, nd, n_qtiles, units_per_bh, units, pair, nsb;
+  int N, mask, window, nd, n_qtiles, units_per_bh, units, nsb;
   // paged K/V: k, v are [pool pages, H, pg_page, d] pools (pg_page 16 or
   // 64 tokens); (sequence s, query block b) reads the page list
   // pg_table + s * pg_stride_s + b * pg_stride_b and its length
@@ -380,8 +380,7 @@ struct QTile {
     RowSpans sp;
     if constexpr (PG) {
       // keys [0, hi(row)]: causal prefill rows sit at positions len - N + row
-      // seq = bh / H, from the caller: the quotient's intermediates would
-      // otherwise stay live across a paired tile's loop
+      // seq = bh / H, from the caller (computed once, in the kernel's entry)
       const int s = seq;
       pg_h = bh - s * p.H;
       const int32_t* list = p.pg_table + (size_t)s * p.pg_stride_s + (size_t)qt * p.pg_stride_b;
@@ -1381,9 +1380,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
   bh = __builtin_amdgcn_readfirstlane(bh);
   w = __builtin_amdgcn_readfirstlane(w);
-  // the longer Q tile first; Q is loaded before the tile stream's first DMAs,
-  // so the two latencies overlap
-  const int ta = w, tb = p.n_qtiles - 1 - w;
+  // unit w is Q tile n_qtiles - 1 - w: the costlier tiles come first in
+  // the orders that rank them
+  const int tile = p.n_qtiles - 1 - w;
   const int seq = PG ? __builtin_amdgcn_readfirstlane(bh / p.H) : 0;   // paged: the sequence
   {
     // with the ordering's LDS copy of the document offsets, the spans are
@@ -1391,7 +1390,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // round trips per workgroup); a barrier then frees the LDS for the ring
     const bool lds_offs = p.order == ORDER_DOC;
     const bool early = !FP8 && !PG && !lds_offs;
-    QTile<D, FP8, OUT_F32, PG, V8, KSPLIT> a(p, smem, bh, tb, lds_offs ? (const int32_t*)(smem + 2 * NT * sizeof(int)) : p.doc,
+    QTile<D, FP8, OUT_F32, PG, V8, KSPLIT> a(p, smem, bh, tile, lds_offs ? (const int32_t*)(smem + 2 * NT * sizeof(int)) : p.doc,
                                      early, part, seq);
     if (!early) {
       a.load_q();
@@ -1400,20 +1399,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
     a.loop();
     a.epilogue();
-  }
-  if (p.pair && ta != tb) {
-    // the first tile's loop ended with every wave past its last LDS read
-    // opaque copies: products of these the first tile's set-up formed are
-    // recomputed here rather than held (and spilled) across its loop
-    int bh_b = bh, seq_b = seq;
-    asm volatile("" : "+s"(bh_b), "+s"(seq_b));
-    QTile<D, FP8, OUT_F32, PG, V8, KSPLIT> b(p, smem, bh_b, ta, p.doc, !FP8 && !PG, -1, seq_b);
-    if (FP8 || PG) {
-      b.load_q();
-      b.start_stream();
-    }
-    b.loop();
-    b.epilogue();
   }
 }
 
@@ -1485,7 +1470,7 @@ hipError_t launch_p(Params& p, int BH, hipStream_t stream) {
     hipLaunchKernelGGL((split_combine_kernel<D, OUT_F32>), dim3(BH * p.n_split), dim3(NT), 0, stream, p);
     return hipGetLastError();
   }
-  p.units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
+  p.units_per_bh = p.n_qtiles;
   p.units = BH * p.units_per_bh;
   const int grid = round_up8(p.units);
   hipLaunchKernelGGL((fwd_mfma_kernel<D, FP8, OUT_F32, PG, V8, KSPLIT>), dim3(grid), dim3(NT), 0, stream, p);
@@ -1623,15 +1608,17 @@ hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
   p.pg_causal = a.causal ? 1 : 0;
   p.pg_page = a.page_size;
   p.pg_cap = a.max_pages * a.page_size;
-  p.pair = p.pg_causal;
-  const int units_per_bh = p.pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles;
-  // cross-attention lists keep the natural order: ranking them (by length)
-  // measured slower with lists of about equal length, since a list's heads
-  // then run side by side instead of each head's blocks sharing an XCD
+  // causal prefill: single Q tiles, sequences ranked by length and each
+  // sequence's tiles costliest first (pairs of tiles t and T-1-t per
+  // workgroup measured 9-11% slower: the two workgroups of a CU share it
+  // unevenly). Cross-attention lists keep the natural order: ranking them
+  // (by length) measured slower with lists of about equal length, since a
+  // list's heads then run side by side instead of each head's blocks
+  // sharing an XCD
   if (a.causal && a.S <= NT) {
     p.order = ORDER_SEQ;
     p.groups = a.S;
-    p.per_group = a.H * units_per_bh;
+    p.per_group = a.H * p.n_qtiles;
   }
   if (a.page_size == kPrefillSmallPage) return launch_p<D, false, OUT_F32, kPrefillSmallPage>(p, a.S * a.H, stream);
   return launch_p<D, false, OUT_F32, kPrefillPageSize>(p, a.S * a.H, stream);
