@@ -315,7 +315,11 @@ attn_status attn_prefill_paged(const void* q, const void* k_pool, const void* v_
  *   page_table : [S, ceil(q_len / 128), max_pages] int32 (device).
  *   kv_lens : [S, ceil(q_len / 128)] int32 (device), 0 <= kv_lens <= max_pages * page_size;
  *            a block with no key gets O = 0 and LSE = -inf.
- * Device contents are handled as for attn_prefill_paged.
+ * Device contents are handled as for attn_prefill_paged. The keys of a block
+ * form a set, so the kernel visits the whole pages among its first 256 list
+ * entries in ascending id order (blocks of one head that share pages then
+ * read them from the L2 together); the result equals the list order's up to
+ * fp32 rounding, and does not depend on how those pages are ordered.
  */
 attn_status attn_cross_paged(const void* q, const void* k_pool, const void* v_pool,
                              const int32_t* page_table, const int32_t* kv_lens, void* o,

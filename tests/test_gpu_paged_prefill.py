@@ -133,6 +133,53 @@ def test_cross_paged_full_size_sampled():
     say(f"{w.name}: sampled rows match")
 
 
+@pytest.mark.parametrize("page", [64, 16])
+def test_cross_paged_repeats_long_lists_and_page_order(page):
+    """A list is a multiset of keys, so the kernel may visit its whole pages
+    in any order (it sorts them by id): lists that repeat pages, lists longer
+    than the part that is reordered (300 pages of 16 tokens), and lengths
+    that end inside the list or inside a page, against the oracle; and a
+    permutation of each list's whole pages (the partial last page left in
+    place) gives the same output bit for bit."""
+    S, H, q_len, d, pool = 2, 2, 256, 128, 40
+    per = 300 if page == 16 else 70
+    base = wl.paged_cross_inputs(S, H, d, q_len, pool, 8, seed=71 + page, page_size=page, spare=3)
+    rng = np.random.default_rng(72 + page)
+    nqb = -(-q_len // 128)
+    table = rng.integers(0, pool, size=(S, nqb, per)).astype(np.int32)
+    lens = np.array([[per * page, per * page - page // 2], [37 * page + 5, 3 * page]], dtype=np.int32)
+    for s in range(S):
+        for b in range(nqb):
+            used = -(-int(lens[s, b]) // page)
+            table[s, b, used:] = pool + rng.integers(0, 3, size=per - used)   # NaN pages, never read
+    inp = wl.CrossInputs(q=base.q, k_pool=base.k_pool, v_pool=base.v_pool, page_table=torch.from_numpy(table),
+                         kv_lens=torch.from_numpy(lens), page_size=page, q_block=128)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _cross(inp, torch.float32, scale)
+    ref, ref_lse = oracle.cross(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
+                                table, lens, scale, page_size=page)
+    check_close(to_np(o), ref, False, what=f"repeats page={page}")
+    check_lse(to_np(lse), ref_lse)
+    perm = table.copy()
+    for s in range(S):
+        for b in range(nqb):
+            full = int(lens[s, b]) // page
+            perm[s, b, :full] = rng.permutation(perm[s, b, :full])
+    inp2 = wl.CrossInputs(q=base.q, k_pool=base.k_pool, v_pool=base.v_pool, page_table=torch.from_numpy(perm),
+                          kv_lens=torch.from_numpy(lens), page_size=page, q_block=128)
+    o2, lse2 = _cross(inp2, torch.float32, scale)
+    # the kernel orders the first 256 entries of a list; past them the order
+    # is the caller's, so only lists of at most 256 whole pages match exactly
+    for s in range(S):
+        for b in range(nqb):
+            rows = slice(128 * b, min(q_len, 128 * (b + 1)))
+            if int(lens[s, b]) // page <= 256:
+                assert torch.equal(o2[s, :, rows], o[s, :, rows]), (s, b)
+                assert torch.equal(lse2[s, :, rows], lse[s, :, rows]), (s, b)
+            else:
+                check_close(to_np(o2[s, :, rows]), ref[s, :, rows], False, what=f"permuted long list {(s, b)}")
+
+
 def test_prefill_paged_one_row_matches_decode():
     """q_len = 1 is a decode: the fused prefill kernel and the decode oracle agree."""
     inp = wl.paged_inputs(4, 2, 128, 1, 3000, seed=47, page_size=64, spare=2, q_rows=1)

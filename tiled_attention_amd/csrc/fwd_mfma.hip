@@ -199,7 +199,9 @@ enum UnitOrder {
   ORDER_SEQ = 2,     // groups = sequences of a paged prefill, costed by length; per group: heads x units
   ORDER_TILES = 3,   // one Q tile per unit, tile-major from the last tile down (costs never fall with
                      // the tile index for these masks), heads innermost so a head stays on one XCD
-  ORDER_SPLIT = 4    // as ORDER_TILES, with the costliest tiles split into two key ranges (unit_tab)
+  ORDER_SPLIT = 4,   // as ORDER_TILES, with the costliest tiles split into two key ranges (unit_tab)
+  ORDER_HEADS = 5    // paged cross-attention: head-major (per_group = sequences x query blocks), each XCD
+                     // taking a contiguous run, so the blocks that read one head's pages share an L2
 };
 constexpr int kKeySplitMinN = 4096;   // bf16 d = 64: the key-split layout from this length
 constexpr int kOrderMaxDocs = 8192;  // document offsets staged in LDS for the costing (and the LDS
@@ -275,6 +277,25 @@ struct TileStream {
     return (i32x4){(int)(uint32_t)base, (int)(uint32_t)(base >> 32), n, kBufferFlags};
   }
 };
+
+// Sorts the first min(n, NT) page ids of an LDS list into ascending order
+// (equal ids keep their order; the rest of the list is left as it is), by
+// rank: each thread counts the entries that precede its own. Called by the
+// whole workgroup; ends with a barrier.
+constexpr int kSortedPages = NT;
+__device__ void sort_ids(int* ids, int n) {
+  n = min(n, kSortedPages);
+  const int i = threadIdx.x;
+  const int key = i < n ? ids[i] : 0;
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const int x = ids[j];
+    rank += (x < key) | ((x == key) & (j < i));
+  }
+  __syncthreads();
+  if (i < n) ids[rank] = key;
+  __syncthreads();
+}
 
 template <int D, bool FP8, bool OUT_F32, int PG, bool V8, bool KSPLIT>
 struct QTile {
@@ -402,6 +423,11 @@ struct QTile {
       const int n_ids = min(NK * (BN / PG), p.pg_max);   // PG: the page size
       for (int i = tid; i < n_ids; i += NT) ids[i] = min(max(list[i], 0), p.pg_pool - 1);
       __syncthreads();
+      // a cross-attention list is a set of keys, so its whole pages may be
+      // visited in any order: ascending ids let the blocks of one head that
+      // list the same page (running side by side on one XCD) read it close
+      // together in time, from the L2. The partial last page stays last
+      if (!p.pg_causal) sort_ids(ids, min(pg_len / PG, n_ids));
       pg_ids = ids;
       pool_k = (uint64_t)(uintptr_t)p.k;
       pool_v = (uint64_t)(uintptr_t)p.v;
@@ -1367,6 +1393,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       w = p.n_qtiles - 1 - min(e & 0xfff, p.n_qtiles - 1);
       part = (e >> 12) & 1 ? (e >> 13) & 1 : -1;
     }
+  } else if (p.order == ORDER_HEADS) {
+    const int u = xcd_unit(blockIdx.x, gridDim.x);
+    if (u >= p.units) return;
+    const int h = u / p.per_group;
+    const int r = u - h * p.per_group;
+    const int s = r / p.n_qtiles;
+    bh = s * p.H + h;
+    w = r - s * p.n_qtiles;
   } else if (p.order != ORDER_NONE) {
     // ranks follow workgroup ids (the dispatch order); each XCD takes every 8th
     const int u = blockIdx.x;
@@ -1611,14 +1645,16 @@ hipError_t launch_pg(const PagedFwdArgs& a, hipStream_t stream) {
   // causal prefill: single Q tiles, sequences ranked by length and each
   // sequence's tiles costliest first (pairs of tiles t and T-1-t per
   // workgroup measured 9-11% slower: the two workgroups of a CU share it
-  // unevenly). Cross-attention lists keep the natural order: ranking them
-  // (by length) measured slower with lists of about equal length, since a
-  // list's heads then run side by side instead of each head's blocks
-  // sharing an XCD
+  // unevenly). Cross-attention: head-major, so that the blocks which read
+  // one head's pages run side by side on one XCD (ranking the lists by
+  // length measured slower with lists of about equal length)
   if (a.causal && a.S <= NT) {
     p.order = ORDER_SEQ;
     p.groups = a.S;
     p.per_group = a.H * p.n_qtiles;
+  } else if (!a.causal) {
+    p.order = ORDER_HEADS;
+    p.per_group = a.S * p.n_qtiles;
   }
   if (a.page_size == kPrefillSmallPage) return launch_p<D, false, OUT_F32, kPrefillSmallPage>(p, a.S * a.H, stream);
   return launch_p<D, false, OUT_F32, kPrefillPageSize>(p, a.S * a.H, stream);
