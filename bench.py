@@ -594,7 +594,7 @@ def main():
     digest = kernel_source_digest()
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
             "frac": round(achieved / peak, 4), "traffic": traffic_for(digest) if main_key == 2 else None,
-            "kernel": ("fwd_mfma_kernel<64, false, false, 0, false> (d=64, bf16 in and out, causal)"
+            "kernel": ("fwd_mfma_kernel<64, false, false, 0, false, false> (d=64, bf16 in and out, causal)"
                        if main_key == 2 else f"workload {main_key}"),
             "kernel_avg_ms": round(avg_ms, 5), "kernel_median_ms": round(med_ms, 5), "kernel_min_ms": round(min_ms, 5),
             "algorithmic_flops_per_launch": wk.flops, "kernel_source_digest": digest}
