@@ -316,10 +316,11 @@ class PagedCross:
 
 
 def event_time_ms(step, reps, warmup=3, settle_ms=30.0):
-    """Average duration of one step from HIP events on the launch stream,
-    after `warmup` calls and then enough further calls to keep the GPU busy
-    for about settle_ms (at most 300): a workload's first launches run slower
-    (clock ramp, first touches of its buffers)."""
+    """Average, median, minimum and 90th-percentile duration (ms) of one step
+    from HIP events on the launch stream, after `warmup` calls and then
+    enough further calls to keep the GPU busy for about settle_ms (at most
+    300): a workload's first launches run slower (clock ramp, first touches
+    of its buffers)."""
     import torch
     for _ in range(warmup):
         step()
@@ -339,7 +340,39 @@ def event_time_ms(step, reps, warmup=3, settle_ms=30.0):
         ends[i].record()
     torch.cuda.synchronize()
     times = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    return sum(times) / len(times), times[len(times) // 2], times[0]
+    return sum(times) / len(times), times[len(times) // 2], times[0], times[min(len(times) - 1, (9 * len(times)) // 10)]
+
+
+def environment():
+    """ROCm, HIP and torch versions and the device name."""
+    import torch
+    env = {"torch": torch.__version__, "hip": torch.version.hip, "device": torch.cuda.get_device_name(0)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    return env
+
+
+def smi_snapshot():
+    """The GPUs' current clocks and power as rocm-smi reports them ({card:
+    {field: value}} for the fields naming a clock or power), or the reason
+    they could not be read. Read-only; runs rocm-smi as a child process."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        data = json.loads(r.stdout)
+    except Exception as e:  # no rocm-smi, no JSON, or a time-out: say so in the line
+        return {"error": f"{type(e).__name__}: {str(e)[:160]}"}
+    out = {}
+    for card, fields in data.items():
+        if isinstance(fields, dict):
+            keep = {k: v for k, v in fields.items() if any(t in k.lower() for t in ("sclk", "mclk", "fclk", "power"))}
+            if keep:
+                out[card] = keep
+    return out
 
 
 def _threads():
@@ -481,7 +514,7 @@ def seq_len_sweep(torch, A):
                            for _ in range(3))
                 o = torch.empty_like(q)
                 step = lambda: A.attn_fwd(q, k, v, o, 1.0 / math.sqrt(d), mask)
-                ms, _, _ = event_time_ms(step, 20 if N <= 8192 else 5)
+                ms = event_time_ms(step, 20 if N <= 8192 else 5)[0]
                 pairs = N * (N + 1) / 2 if mask == "causal" else N * N
                 tf = 4.0 * d * B * H * pairs / ms / 1e9
                 rows.append({"d": d, "mask": mask, "N": N, "B": B, "H": H, "ms": round(ms, 5),
@@ -499,8 +532,8 @@ def seq_len_sweep(torch, A):
         o = torch.empty_like(q)
         nb = A.attn_fwd_split_workspace_size(B, H, N, d, "bf16", "causal")
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
-        ms_f, _, _ = event_time_ms(lambda: A.attn_fwd(q, k, v, o, 1.0 / math.sqrt(d), "causal"), 20)
-        ms_s, _, _ = event_time_ms(lambda: A.attn_fwd_split(q, k, v, o, 1.0 / math.sqrt(d), "causal", workspace=ws), 20)
+        ms_f = event_time_ms(lambda: A.attn_fwd(q, k, v, o, 1.0 / math.sqrt(d), "causal"), 20)[0]
+        ms_s = event_time_ms(lambda: A.attn_fwd_split(q, k, v, o, 1.0 / math.sqrt(d), "causal", workspace=ws), 20)[0]
         fl = 4.0 * d * B * H * N * (N + 1) / 2
         split_rows.append({"B": B, "H": H, "N": N, "d": d, "workspace_bytes": nb, "fwd_ms": round(ms_f, 5),
                            "split_ms": round(ms_s, 5), "fwd_frac": round(fl / ms_f / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -566,6 +599,7 @@ def main():
     main_key = args.workload if args.only_main else 2
     log(f"bench: preparing workload {main_key}")
     wk = make(main_key)
+    smi_before = smi_snapshot()
     settled = settle(wk.step)
     for _ in range(args.warmup):
         wk.step()
@@ -575,8 +609,9 @@ def main():
         wk.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    smi_after = smi_snapshot()
     ms_step = wall * 1e3 / args.steps
-    avg_ms, med_ms, min_ms = event_time_ms(wk.step, max(args.steps, 20))
+    avg_ms, med_ms, min_ms, p90_ms = event_time_ms(wk.step, max(args.steps, 20))
     log(f"bench: workload {main_key}: wall {ms_step:.4f} ms/step, kernel avg {avg_ms:.4f} ms")
 
     if isinstance(wk, Paged):
@@ -596,7 +631,7 @@ def main():
             "frac": round(achieved / peak, 4), "traffic": traffic_for(digest) if main_key == 2 else None,
             "kernel": ("fwd_mfma_kernel<64, false, false, 0, false, false> (d=64, bf16 in and out, causal)"
                        if main_key == 2 else f"workload {main_key}"),
-            "kernel_avg_ms": round(avg_ms, 5), "kernel_median_ms": round(med_ms, 5), "kernel_min_ms": round(min_ms, 5),
+            "kernel_avg_ms": round(avg_ms, 5), "kernel_median_ms": round(med_ms, 5), "kernel_min_ms": round(min_ms, 5), "kernel_p90_ms": round(p90_ms, 5),
             "algorithmic_flops_per_launch": wk.flops, "kernel_source_digest": digest}
     ghz = clock_for(digest) if main_key == 2 else None
     if ghz:
@@ -611,6 +646,9 @@ def main():
         "vs_baseline": None, "dtype": "fp8e4m3" if isinstance(wk, Fp8Full) else "fp8e4m3+bf16" if isinstance(wk, Fp8) else "bf16",
         "data": "synthetic", "config": wk.describe(), "roofline": roof,
         "settle_launches": settled,
+        # versions, and rocm-smi's clocks and power before the settling
+        # launches and right after the timed steps
+        "environment": dict(environment(), smi_before=smi_before, smi_after_timed=smi_after),
     }
 
     if not args.only_main:
@@ -623,9 +661,9 @@ def main():
                           (11, 20), (12, 20), (13, 20), (14, 20), (15, 20)):
             log(f"bench: workload {key}")
             o = make(key)
-            avg, med, mn = event_time_ms(o.step, reps)
+            avg, med, mn, p90 = event_time_ms(o.step, reps)
             entry = {"config": o.describe(), "ms_avg": round(avg, 5), "ms_median": round(med, 5),
-                     "ms_min": round(mn, 5)}
+                     "ms_min": round(mn, 5), "ms_p90": round(p90, 5)}
             if isinstance(o, Paged):
                 gbs = o.bytes / (avg * 1e-3) / 1e9
                 entry.update({"value": round(gbs, 1), "unit": "GB/s", "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
@@ -648,9 +686,9 @@ def main():
             if isinstance(o, PagedPrefill):
                 # "Optimizing Triton kernels ...", Pattern C: gather, then
                 # attend over the dense copy, against the fused kernel
-                g_avg, _, _ = event_time_ms(o.gather, reps)
-                a_avg, _, _ = event_time_ms(o.attend_gathered, reps)
-                t_avg, _, _ = event_time_ms(o.two_stage, reps)
+                g_avg = event_time_ms(o.gather, reps)[0]
+                a_avg = event_time_ms(o.attend_gathered, reps)[0]
+                t_avg = event_time_ms(o.two_stage, reps)[0]
                 entry["two_stage_gather_ms"] = round(g_avg, 5)
                 entry["two_stage_gather_GBps"] = round(o.gather_bytes / (g_avg * 1e-3) / 1e9, 1)
                 entry["two_stage_attend_ms"] = round(a_avg, 5)
