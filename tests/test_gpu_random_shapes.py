@@ -1,0 +1,83 @@
+"""A seeded sweep of random small problems through attn_fwd and
+attn_fwd_split, against the oracle element by element: every mask kind, both
+input and output types, d = 64 and 128, lengths that are not tile multiples,
+random windows and document layouts. The shapes are drawn once from a fixed
+seed, so a failure names a case that can be run again."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check_close, check_lse, cuda, say, to_np
+from tiled_attention_amd import _lib as A
+from tiled_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+MASK_KINDS = ["none", "causal", "sliding", "band", "prefix_lm", "document", "document_causal"]
+
+
+def _draw_cases(n, seed=20261):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        mask = MASK_KINDS[i % len(MASK_KINDS)]
+        N = int(rng.integers(1, 1300))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        d = int(rng.choice([64, 128]))
+        in_f32 = bool(rng.random() < 0.25)
+        out_f32 = bool(rng.random() < 0.5)
+        window = 0
+        if mask == "sliding":
+            window = int(rng.integers(1, N + 40))
+        elif mask == "band":
+            window = int(rng.integers(0, N + 40))
+        elif mask == "prefix_lm":
+            window = int(rng.integers(0, N + 40))
+        split = mask in ("causal", "prefix_lm") and not in_f32 and rng.random() < 0.5
+        cases.append((i, B, H, N, d, mask, window, in_f32, out_f32, split))
+    return cases
+
+
+CASES = _draw_cases(140)
+
+
+def _offsets(N, seed):
+    rng = np.random.default_rng(seed)
+    cuts = sorted(set(rng.integers(0, N + 1, size=int(rng.integers(0, 6))).tolist()))
+    return np.array([0] + cuts + [N], dtype=np.int32)    # empty documents allowed
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_random_shape_elementwise(case):
+    i, B, H, N, d, mask, window, in_f32, out_f32, split = case
+    say(f"random shape {case}")
+    seed = 9000 + i
+    q, k, v = wl.dense_inputs(B, H, N, d, seed=seed)
+    if in_f32:
+        qi, ki, vi = (torch.from_numpy(x) for x in (q, k, v))
+        qr, kr, vr = q.astype(np.float64), k.astype(np.float64), v.astype(np.float64)
+    else:
+        qi, ki, vi = wl.to_bf16(q), wl.to_bf16(k), wl.to_bf16(v)
+        qr, kr, vr = wl.bf16_to_f64(qi), wl.bf16_to_f64(ki), wl.bf16_to_f64(vi)
+    offs = _offsets(N, seed) if mask.startswith("document") else None
+    doc = None if offs is None else torch.from_numpy(offs).cuda()
+    scale = 1.0 / math.sqrt(d)
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    if split:
+        ws_bytes = A.attn_fwd_split_workspace_size(B, H, N, d, "bf16", mask, window)
+        ws = torch.full((max(ws_bytes, 1),), 0xFF, dtype=torch.uint8, device="cuda") if ws_bytes else None
+        A.attn_fwd_split(cuda(qi), cuda(ki), cuda(vi), o, scale, mask, window, lse=lse, workspace=ws)
+    else:
+        A.attn_fwd(cuda(qi), cuda(ki), cuda(vi), o, scale, mask, window, doc_offsets=doc, lse=lse)
+    torch.cuda.synchronize()
+    win = window if mask in ("sliding", "band", "prefix_lm") else None
+    ref, ref_lse = oracle.attention(qr, kr, vr, scale, mask, win, doc_offsets=offs)
+    err = check_close(to_np(o), ref, not out_f32, what=str(case))
+    if in_f32 and out_f32:
+        assert err <= 1e-4, f"{case}: fp32 path max abs err {err:.3g}"
+    check_lse(to_np(lse), ref_lse, tol=1e-4 if in_f32 else None, what=str(case))
