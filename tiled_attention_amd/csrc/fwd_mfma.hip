@@ -1382,6 +1382,11 @@ template <int D, bool FP8, bool OUT_F32, int PG, bool V8, bool KSPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg<D, FP8, V8>::LDS + (PG ? 4 * kPrefillMaxPages : 0)];
   int bh, w, part = -1;
+  // the set-up's kernel arguments in one batch of loads before the first
+  // branch: the compiler otherwise loads each field where it is first used,
+  // each behind a wait of its own (a chain of scalar round trips)
+  asm volatile("" ::"s"(p.order), "s"(p.units), "s"(p.per_group), "s"(p.n_qtiles), "s"(p.N), "s"(p.mask),
+               "s"(p.window), "s"(p.nd), "s"(p.q), "s"(p.k), "s"(p.v), "s"(p.H), "s"(p.o), "s"(p.lse));
   if (p.order == ORDER_TILES || p.order == ORDER_SPLIT) {
     const int u = blockIdx.x;
     if (u >= p.units) return;
