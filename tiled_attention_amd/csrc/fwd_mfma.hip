@@ -506,6 +506,7 @@ struct QTile {
     f_lo = min(max(f_lo - t_lo, 0), NK);
     f_hi = min(max(f_hi - t_lo, f_lo), NK);
     qscale = 1.f;
+    if constexpr (V8) P8[0] = P8[1] = (i32x8){};   // defined words for the conversions to start from
     if constexpr (FP8) qscale = p.q_scale[bh * p.nsb + m0 / 128];
 
     // K read of k-step t: lane l32 supplies S^T row l32 of block 0 (block 1:
@@ -840,10 +841,12 @@ struct QTile {
         if constexpr (!V8) P[B][q][j] = (__bf16)e[8 * q + j];
       }
     if constexpr (V8) {
-      // byte k of the B operand is e[k] (key 32 hl + k), rounded to E4M3
+      // byte k of the B operand is e[k] (key 32 hl + k), rounded to E4M3; the
+      // two conversions write the low and the high half of the word, so its
+      // starting value does not matter (and takes no instruction to set)
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        int d = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], P8[B][w], false);
         P8[B][w] = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], d, true);
       }
     }
