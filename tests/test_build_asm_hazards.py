@@ -9,11 +9,18 @@ half read was the clamp's SCC: the tile address gained 4 GiB and the GPU took
 a memory fault. This test scans every kernel for an SCC read that follows an
 SCC-writing asm block with no SCC write in between."""
 
+import functools
 import re
 
 import pytest
 
 from tiled_attention_amd import build
+
+
+@functools.lru_cache(maxsize=None)
+def _assembly(src):
+    # one compile per source for all the scans of this module
+    return build.assembly(src)
 
 SCC_WRITERS = ("s_cmp", "s_min_", "s_max_", "s_add_u32", "s_sub_u32", "s_add_i32", "s_sub_i32", "s_and_",
                "s_or_", "s_xor_", "s_andn2_", "s_orn2_", "s_nand_", "s_nor_", "s_xnor_", "s_lshl", "s_lshr",
@@ -66,7 +73,7 @@ def test_scanner_finds_the_hazard_it_is_for():
 
 @pytest.mark.parametrize("src", [s for s in build.SOURCES if s.endswith(".hip")])
 def test_no_scc_read_after_scc_writing_asm(src):
-    assert scc_hazards(build.assembly(src)) == []
+    assert scc_hazards(_assembly(src)) == []
 
 
 # The Q tile is loaded with inline-asm global loads that the compiler does not
@@ -164,4 +171,4 @@ def test_load_scanner_finds_a_copy_before_the_wait():
 
 
 def test_q_registers_untouched_until_their_wait():
-    assert asm_load_hazards(build.assembly("fwd_mfma.hip")) == []
+    assert asm_load_hazards(_assembly("fwd_mfma.hip")) == []
