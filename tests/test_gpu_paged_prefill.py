@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from parity import check_lse, LSE_TOL_MFMA, check_close, sample_rows, say, to_np
+from parity import check_lse, LSE_TOL_MFMA, check_close, cuda, sample_rows, say, to_np
 from tiled_attention_amd import _lib as A
 from tiled_attention_amd import workloads as wl
 
@@ -252,3 +252,25 @@ def test_two_stage_route_equals_fused(page):
     torch.cuda.synchronize()
     assert torch.isfinite(fused.float()).all()
     assert torch.equal(o2.view(torch.int16), fused.view(torch.int16))
+
+
+@pytest.mark.parametrize("page", [64, 16])
+def test_cross_out_of_contract_lists_stay_in_bounds(page):
+    """Page ids outside [0, num_pages) and lengths outside [0, max_pages *
+    page] break the caller's contract; the kernel clamps both (before it
+    orders a list's pages), so the call completes (results unspecified there)
+    and a valid block beside the broken ones gives its exact result."""
+    S, H, q_len, d, pool, per = 2, 2, 384, 128, 30, 12
+    inp = wl.paged_cross_inputs(S, H, d, q_len, pool, per, seed=91 + page, page_size=page, spare=3)
+    table, lens = inp.page_table.clone(), inp.kv_lens.clone()
+    num_pages = inp.k_pool.shape[0]
+    table[0, 1, 0] = -1                        # an id below the pool
+    table[0, 2, :] = num_pages + 7             # every id past the pool
+    lens[0, 2] = per * page + 100              # ... and a length past its list
+    lens[1, 1] = -3                            # a negative length
+    o = torch.zeros(inp.q.shape, dtype=torch.float32, device="cuda")
+    A.attn_cross_paged(cuda(inp.q), cuda(inp.k_pool), cuda(inp.v_pool), cuda(table), cuda(lens), o, 0.1)
+    torch.cuda.synchronize()
+    ref, _ = oracle.cross(wl.bf16_to_f64(inp.q), inp.k_pool.float().numpy(), inp.v_pool.float().numpy(),
+                          inp.page_table.numpy(), inp.kv_lens.numpy(), 0.1, page_size=page)
+    check_close(to_np(o[1, :, 0:128]), ref[1, :, 0:128], False, what="valid block beside broken ones")
