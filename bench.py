@@ -377,6 +377,35 @@ def smi_snapshot():
     return out
 
 
+def batch_time_ms(step, reps, groups=10, warmup=3, settle_ms=30.0):
+    """Average, median, minimum and 90th-percentile time (ms) per launch,
+    from `groups` groups of back-to-back launches, each group between one
+    pair of HIP events on the launch stream (so the events' own time is
+    spread over the group), after the same settling as event_time_ms."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    one_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(min(300, int(settle_ms / max(one_ms, 1e-3)))):
+        step()
+    torch.cuda.synchronize()
+    n = max(1, reps // groups)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(groups)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(groups)]
+    for g in range(groups):
+        starts[g].record()
+        for _ in range(n):
+            step()
+        ends[g].record()
+    torch.cuda.synchronize()
+    times = sorted(s_.elapsed_time(e) / n for s_, e in zip(starts, ends))
+    return sum(times) / len(times), times[len(times) // 2], times[0], times[min(len(times) - 1, (9 * len(times)) // 10)]
+
+
 def _threads():
     from threadpoolctl import threadpool_info
     return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
@@ -516,7 +545,7 @@ def seq_len_sweep(torch, A):
                            for _ in range(3))
                 o = torch.empty_like(q)
                 step = lambda: A.attn_fwd(q, k, v, o, 1.0 / math.sqrt(d), mask)
-                ms = event_time_ms(step, 20 if N <= 8192 else 5)[0]
+                ms = batch_time_ms(step, 40 if N <= 8192 else 10, groups=5)[0]
                 pairs = N * (N + 1) / 2 if mask == "causal" else N * N
                 tf = 4.0 * d * B * H * pairs / ms / 1e9
                 rows.append({"d": d, "mask": mask, "N": N, "B": B, "H": H, "ms": round(ms, 5),
@@ -534,8 +563,8 @@ def seq_len_sweep(torch, A):
         o = torch.empty_like(q)
         nb = A.attn_fwd_split_workspace_size(B, H, N, d, "bf16", "causal")
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
-        ms_f = event_time_ms(lambda: A.attn_fwd(q, k, v, o, 1.0 / math.sqrt(d), "causal"), 20)[0]
-        ms_s = event_time_ms(lambda: A.attn_fwd_split(q, k, v, o, 1.0 / math.sqrt(d), "causal", workspace=ws), 20)[0]
+        ms_f = batch_time_ms(lambda: A.attn_fwd(q, k, v, o, 1.0 / math.sqrt(d), "causal"), 40, groups=5)[0]
+        ms_s = batch_time_ms(lambda: A.attn_fwd_split(q, k, v, o, 1.0 / math.sqrt(d), "causal", workspace=ws), 40, groups=5)[0]
         fl = 4.0 * d * B * H * N * (N + 1) / 2
         split_rows.append({"B": B, "H": H, "N": N, "d": d, "workspace_bytes": nb, "fwd_ms": round(ms_f, 5),
                            "split_ms": round(ms_s, 5), "fwd_frac": round(fl / ms_f / 1e9 / PEAK_BF16_TFLOPS, 4),
@@ -675,7 +704,7 @@ def main():
                           (11, 20), (12, 20), (13, 20), (14, 20), (15, 20)):
             log(f"bench: workload {key}")
             o = make(key)
-            avg, med, mn, p90 = event_time_ms(o.step, reps)
+            avg, med, mn, p90 = batch_time_ms(o.step, reps)
             entry = {"config": o.describe(), "ms_avg": round(avg, 5), "ms_median": round(med, 5),
                      "ms_min": round(mn, 5), "ms_p90": round(p90, 5)}
             if isinstance(o, Paged):
@@ -700,9 +729,9 @@ def main():
             if isinstance(o, PagedPrefill):
                 # "Optimizing Triton kernels ...", Pattern C: gather, then
                 # attend over the dense copy, against the fused kernel
-                g_avg = event_time_ms(o.gather, reps)[0]
-                a_avg = event_time_ms(o.attend_gathered, reps)[0]
-                t_avg = event_time_ms(o.two_stage, reps)[0]
+                g_avg = batch_time_ms(o.gather, reps)[0]
+                a_avg = batch_time_ms(o.attend_gathered, reps)[0]
+                t_avg = batch_time_ms(o.two_stage, reps)[0]
                 entry["two_stage_gather_ms"] = round(g_avg, 5)
                 entry["two_stage_gather_GBps"] = round(o.gather_bytes / (g_avg * 1e-3) / 1e9, 1)
                 entry["two_stage_attend_ms"] = round(a_avg, 5)
