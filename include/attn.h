@@ -24,8 +24,10 @@
  *   - Base pointers must be 16-byte aligned. Outputs must not alias inputs.
  *   - Tensors are dense, row-major, innermost dimension last.
  *   - Sizes: d (head dim) in {64, 128}; N >= 1; B*H*N < 2^31.
- *   - No C++ exception crosses this interface; the library holds no state
- *     and every call is thread-safe.
+ *   - No C++ exception crosses this interface. Every call is thread-safe and
+ *     the library holds no state, with one exception: attn_decode_paged_noalloc
+ *     keeps a fixed device array per GPU (and its address), whose calls race
+ *     when they overlap on one GPU (see there).
  */
 #ifndef TILED_ATTENTION_AMD_ATTN_H
 #define TILED_ATTENTION_AMD_ATTN_H
