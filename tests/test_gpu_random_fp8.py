@@ -4,9 +4,11 @@ dequantised inputs (codes times block scales, exact in fp64): attn_fwd_fp8
 mask kind, d = 64 and 128, lengths that are not block multiples, random
 windows and document layouts, with the outlier inputs of the fp8 workloads.
 The bars are those of the fixed-shape fp8 tests: relative RMSE at most 1e-2
-with bf16 P and 2e-2 with P rounded to e4m3, and the fp8 LSE bound."""
+with bf16 P and 2e-2 with P rounded to e4m3, and the fp8 LSE bound.
+ATTN_SWEEP_SCALE=k draws k times as many cases from the same seed."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -20,12 +22,13 @@ from tiled_attention_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 MASK_KINDS = ["none", "causal", "sliding", "band", "prefix_lm", "document", "document_causal"]
+SCALE = max(1, int(os.environ.get("ATTN_SWEEP_SCALE", "1")))
 
 
 def _cases():
     rng = np.random.default_rng(8080)
     out = []
-    for i in range(28):
+    for i in range(28 * SCALE):
         mask = MASK_KINDS[i % len(MASK_KINDS)]
         N = int(rng.integers(1, 1100))
         B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))

@@ -3,9 +3,12 @@ split-KV decode (with and without a workspace), the fused paged prefill and
 block-sparse paged cross-attention, over 16- and 64-token pages, d = 64 and
 128, random sequence counts, heads, lengths and list sizes. The pools hold NaN
 in every page no sequence or list owns. The shapes are drawn once from a fixed
-seed, so a failure names a case that can be run again."""
+seed, so a failure names a case that can be run again. ATTN_SWEEP_SCALE=k
+draws k times as many cases from the same seeds (the default cases come
+first)."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -18,11 +21,13 @@ from tiled_attention_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
+SCALE = max(1, int(os.environ.get("ATTN_SWEEP_SCALE", "1")))
+
 
 def _decode_cases():
     rng = np.random.default_rng(31337)
     cases = []
-    for i in range(30):
+    for i in range(30 * SCALE):
         S, H = int(rng.integers(1, 10)), int(rng.integers(1, 5))
         d, page = int(rng.choice([64, 128])), int(rng.choice([16, 64]))
         lo = int(rng.integers(1, 3000))
@@ -34,7 +39,7 @@ def _decode_cases():
 def _prefill_cases():
     rng = np.random.default_rng(4242)
     cases = []
-    for i in range(30):
+    for i in range(30 * SCALE):
         S, H = int(rng.integers(1, 6)), int(rng.integers(1, 4))
         d, page = int(rng.choice([64, 128])), int(rng.choice([16, 64]))
         q_len = int(rng.integers(1, 400))
@@ -47,7 +52,7 @@ def _prefill_cases():
 def _cross_cases():
     rng = np.random.default_rng(777)
     cases = []
-    for i in range(30):
+    for i in range(30 * SCALE):
         S, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
         d, page = int(rng.choice([64, 128])), int(rng.choice([16, 64]))
         q_len = int(rng.integers(1, 520))

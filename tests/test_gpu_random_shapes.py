@@ -2,9 +2,13 @@
 attn_fwd_split, against the oracle element by element: every mask kind, both
 input and output types, d = 64 and 128, lengths that are not tile multiples,
 random windows and document layouts. The shapes are drawn once from a fixed
-seed, so a failure names a case that can be run again."""
+seed, so a failure names a case that can be run again. A second, shorter
+sweep takes 1000-6000 tokens, which reaches the bf16 d = 64 key-split layout
+(from 4096 keys) and longer split-key grids. ATTN_SWEEP_SCALE=k draws k times
+as many cases from the same seeds (the default cases come first)."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -42,7 +46,28 @@ def _draw_cases(n, seed=20261):
     return cases
 
 
-CASES = _draw_cases(140)
+def _draw_long_cases(n, seed=20262):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        mask = MASK_KINDS[i % len(MASK_KINDS)]
+        N = int(rng.integers(1000, 6000))
+        H = int(rng.integers(1, 3))
+        d = int(rng.choice([64, 128]))
+        out_f32 = bool(rng.random() < 0.3)
+        window = 0
+        if mask == "sliding":
+            window = int(rng.integers(1, N + 40))
+        elif mask in ("band", "prefix_lm"):
+            window = int(rng.integers(0, N + 40))
+        split = mask in ("causal", "prefix_lm") and (i // len(MASK_KINDS)) % 2 == 0
+        cases.append((1000 + i, 1, H, N, d, mask, window, False, out_f32, split))
+    return cases
+
+
+SCALE = max(1, int(os.environ.get("ATTN_SWEEP_SCALE", "1")))
+CASES = _draw_cases(140 * SCALE)
+LONG_CASES = _draw_long_cases(8 * SCALE)
 
 
 def _offsets(N, seed):
@@ -53,6 +78,15 @@ def _offsets(N, seed):
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_random_shape_elementwise(case):
+    _check(case)
+
+
+@pytest.mark.parametrize("case", LONG_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_random_long_shape_elementwise(case):
+    _check(case)
+
+
+def _check(case):
     i, B, H, N, d, mask, window, in_f32, out_f32, split = case
     say(f"random shape {case}")
     seed = 9000 + i
